@@ -1,0 +1,175 @@
+/*
+ * gkdhead.h - C ABI of libgkdhead, the GKDT parameter-free detection head
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The head turns prompt kernels and dense query features into heatmaps and
+ * keypoints (GKDT-L GGUF model card, huggingface.co/Asher-1/GKD_GGUF,
+ * section "Model"; GKDT paper summary, agihunt.info, pipeline paragraph):
+ *   1. gkd_vkp_pool       Gaussian pooling of support feature fibres around
+ *                         each support keypoint (visual keypoint prototypes);
+ *   2. gkd_kernel_heatmap L2-normalised kernel rows applied as a 1x1
+ *                         convolution to the 4x bilinearly upsampled query
+ *                         features, fused per row over the prompt modalities,
+ *                         optionally with the peak decode fused in;
+ *   3. gkd_peak_decode    per-row argmax of a heatmap, mapped to -1..1, plus
+ *                         the score.
+ *
+ * Conventions shared by every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller, dense
+ *     and row-major in the shape given. Feature maps, kernel rows,
+ *     prototypes and heatmaps must be 16-byte aligned, keypoints and decode
+ *     outputs 4-byte aligned (else GKD_ERR_ALIGN); masks have no
+ *     alignment requirement. The library
+ *     allocates no memory and keeps no state besides a thread-local error
+ *     text, so calls are re-entrant.
+ *   - Calls are asynchronous and ordered on `stream` (0 = the null stream).
+ *     The library never synchronises. Faults inside a kernel surface at the
+ *     caller's next synchronisation as a HIP error.
+ *   - Arguments are validated before anything is launched: on any status
+ *     other than GKD_OK nothing is launched and no output byte is written.
+ *     gkd_last_error() then describes the failure.
+ *   - Outputs must not overlap inputs or each other.
+ *   - B == 0 or R == 0 is an empty batch: GKD_OK, nothing launched.
+ *   - Every element count (e.g. B*R*4H*4W) must be below 2^31.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
+ *   - `flags` is reserved and must be 0 (else GKD_ERR_UNSUPPORTED).
+ */
+#ifndef GKDHEAD_H
+#define GKDHEAD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GKD_ABI_VERSION 1
+
+#ifndef GKD_API
+#define GKD_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    GKD_OK = 0,
+    GKD_ERR_NULL = 1,        /* required pointer NULL, or a pointer group half NULL */
+    GKD_ERR_SHAPE = 2,       /* negative/zero size, or an element count >= 2^31   */
+    GKD_ERR_DTYPE = 3,       /* dtype not one of gkd_dtype                         */
+    GKD_ERR_VALUE = 4,       /* stride or sigma not finite and positive           */
+    GKD_ERR_UNSUPPORTED = 5, /* nonzero flags, or a shape beyond the kernels' limits */
+    GKD_ERR_HIP = 6,         /* the HIP runtime refused a launch                   */
+    GKD_ERR_ALIGN = 7        /* a pointer is not 16-byte aligned                    */
+} gkd_status;
+
+typedef enum {
+    GKD_DTYPE_F32 = 0,  /* IEEE float32 */
+    GKD_DTYPE_BF16 = 1  /* bfloat16 (upper half of a float32) */
+} gkd_dtype;
+
+/* ABI version of the loaded library (GKD_ABI_VERSION). */
+GKD_API int gkd_abi_version(void);
+
+/* Static, never-NULL name of a status code (unknown codes included). */
+GKD_API const char *gkd_status_string(int status);
+
+/* Thread-local detail of the calling thread's last failed call ("" if the
+ * last call succeeded). Valid until the thread's next gkd_* call. */
+GKD_API const char *gkd_last_error(void);
+
+/*
+ * Visual keypoint prototypes (VKP).
+ * GKDT-L GGUF model card, section "Model", "Prompts" bullet: a 1-shot visual
+ * prompt is pooled from the support features with a soft Gaussian over the
+ * feature fibres, sigma = 14 px; the paper summary (agihunt.info, pipeline
+ * paragraph) takes the prototypes from Gaussian heatmaps on the support
+ * image; the reading notes (paper.gecl.asia, "Method") aggregate the support
+ * features near each annotated point.
+ *
+ * For every (b, r) with kpt_valid[b,r] != 0:
+ *   w(i,j)  = exp(-((cx_j - x)^2 + (cy_i - y)^2) / (2 sigma^2)),
+ *             cx_j = (j + 1/2) stride_px, cy_i = (i + 1/2) stride_px
+ *   protos[b,r,c] = sum_ij w(i,j) support[b,c,i,j] / sum_ij w(i,j)
+ * over the whole H x W grid, rounded to `dtype` (bf16: nearest, ties to
+ * even). Rows with kpt_valid == 0 are not written.
+ *
+ *   support    [B,C,H,W] dtype   support feature map
+ *   kpts_px    [B,R,2]   float32 (x, y) in input pixels; the input spans
+ *                                [0, W*stride_px) x [0, H*stride_px)
+ *   kpt_valid  [B,R]     uint8   nonzero = row has a keypoint
+ *   stride_px  > 0, finite (16 for a ViT/16 backbone)
+ *   sigma_px   > 0, finite (14 in the model card)
+ *   protos     [B,R,C]   dtype   output
+ * Limits: C >= 1, H >= 1, W >= 1.
+ */
+GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
+                        const uint8_t *kpt_valid, int B, int C, int H, int W,
+                        int R, float stride_px, float sigma_px,
+                        gkd_dtype dtype, uint32_t flags, void *protos,
+                        hipStream_t stream);
+
+/*
+ * Kernel heatmaps, with the peak decode optionally fused.
+ * GKDT-L GGUF model card, section "Model": the parameter-free head upsamples
+ * the features 4x bilinearly, L2-normalises the kernels, applies them as a
+ * 1x1 convolution and fuses the prompts row by row under a mask, prompt rows
+ * padded to 80; its "Output" bullet takes the per-prompt peak of each
+ * 4H x 4W map as a -1..1 keypoint plus a score. The reading notes
+ * (paper.gecl.asia, "Method") call this a normalised convolution of the
+ * generated kernels with the query features.
+ *
+ * For every (b, r) with mask_vis[b,r] or mask_txt[b,r] set (n = number of
+ * set masks), with u = up4(query[b]) the half-pixel bilinear 4x upsample:
+ *   heatmaps[b,r,y,x] = (1/n) sum_{m set} sum_c k_m[b,r,c] u[c,y,x] / ||k_m[b,r]||
+ * (||k|| is clamped below at 1e-12). Computed at low resolution and then
+ * expanded, which is the same linear map. Rows with no mask set are not
+ * written.
+ *
+ *   query      [B,C,H,W] dtype   query feature map
+ *   kern_vis   [B,R,C]   dtype   visual kernels; mask_vis [B,R] uint8.
+ *                                Both NULL = no visual prompt in the batch.
+ *   kern_txt   [B,R,C]   dtype   text kernels; mask_txt [B,R] uint8.
+ *                                Both NULL = no text prompt in the batch.
+ *                                At least one modality must be given.
+ *   heatmaps   [B,R,4H,4W] float32 output
+ *   peak_idx   [B,R]   int32     optional fused decode (see gkd_peak_decode);
+ *   peak_xy    [B,R,2] float32   all three NULL = no decode, else all three
+ *   peak_score [B,R]   float32   non-NULL. Rows with no mask get the sentinel.
+ * Limits: C >= 1, H >= 1, W >= 1; H*W <= 2304; C <= 2304 (bf16) or
+ * C <= 1152 (f32).
+ */
+GKD_API gkd_status gkd_kernel_heatmap(const void *query, const void *kern_vis,
+                              const uint8_t *mask_vis, const void *kern_txt,
+                              const uint8_t *mask_txt, int B, int C, int H,
+                              int W, int R, gkd_dtype dtype, uint32_t flags,
+                              float *heatmaps, int32_t *peak_idx,
+                              float *peak_xy, float *peak_score,
+                              hipStream_t stream);
+
+/*
+ * Peak decode.
+ * GKDT-L GGUF model card, section "Model", "Output" bullet: each prompt's
+ * heatmap peak becomes a keypoint in the crop's normalised -1..1 frame plus
+ * a confidence score.
+ *
+ * For every (b, r) with row_valid[b,r] != 0 (or every row if row_valid is
+ * NULL): p = the lowest flat index y*Wo + x holding the row's maximum;
+ *   peak_idx   = p
+ *   peak_xy    = ((2x + 1)/Wo - 1, (2y + 1)/Ho - 1)   (cell centres)
+ *   peak_score = heatmaps[b,r,y,x]
+ * Invalid rows get idx -1, xy NaN, score -inf.
+ *
+ *   heatmaps   [B,R,Ho,Wo] float32
+ *   row_valid  [B,R] uint8 or NULL
+ *   peak_idx [B,R] int32, peak_xy [B,R,2] float32, peak_score [B,R] float32
+ * Limits: Ho >= 1, Wo >= 1.
+ */
+GKD_API gkd_status gkd_peak_decode(const float *heatmaps, const uint8_t *row_valid,
+                           int B, int R, int Ho, int Wo, uint32_t flags,
+                           int32_t *peak_idx, float *peak_xy,
+                           float *peak_score, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GKDHEAD_H */

@@ -1,0 +1,183 @@
+"""ctypes binding of libgkdhead (the GKDT detection head on gfx950).
+
+Argument marshalling only: shape/dtype/device checks, output allocation
+with torch, and the call through the C ABI declared in include/gkdhead.h.
+Every step of the computation runs in the library's HIP kernels. There is
+no fallback: if libgkdhead.so is missing or a call fails, this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
+
+GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
+STATUS = {0: "GKD_OK", 1: "GKD_ERR_NULL", 2: "GKD_ERR_SHAPE", 3: "GKD_ERR_DTYPE",
+          4: "GKD_ERR_VALUE", 5: "GKD_ERR_UNSUPPORTED", 6: "GKD_ERR_HIP",
+          7: "GKD_ERR_ALIGN"}
+
+_lib = None
+_P, _I, _U32, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_float
+
+
+class GkdError(RuntimeError):
+    """A gkd_* call returned a non-OK status."""
+
+    def __init__(self, status: int, text: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+
+
+def load():
+    """Load libgkdhead.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import "
+            "__graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.gkd_abi_version.restype = _I
+    lib.gkd_status_string.restype = ctypes.c_char_p
+    lib.gkd_status_string.argtypes = [_I]
+    lib.gkd_last_error.restype = ctypes.c_char_p
+    lib.gkd_vkp_pool.restype = _I
+    lib.gkd_vkp_pool.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _I, _U32,
+                                 _P, _P]
+    lib.gkd_kernel_heatmap.restype = _I
+    lib.gkd_kernel_heatmap.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _U32, _P, _P, _P, _P, _P]
+    lib.gkd_peak_decode.restype = _I
+    lib.gkd_peak_decode.argtypes = [_P, _P, _I, _I, _I, _I, _U32, _P, _P, _P, _P]
+    if lib.gkd_abi_version() != 1:
+        raise ImportError("libgkdhead ABI version mismatch")
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GkdError(status, load().gkd_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GKD_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return GKD_DTYPE_BF16
+    raise TypeError(f"features must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    return t
+
+
+def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
+             stride: float = 16.0, sigma: float = 14.0,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """support [B,C,H,W] (f32|bf16), kpts [B,R,2] f32 px, kpt_valid [B,R] u8
+    -> protos [B,R,C] in the support dtype (rows with kpt_valid == 0 are
+    left as they are in `out`)."""
+    lib = load()
+    _dev(support, "support", ndim=4)
+    B, C, H, W = support.shape
+    _dev(kpts, "kpts", torch.float32, 3)
+    _dev(kpt_valid, "kpt_valid", torch.uint8, 2)
+    R = kpt_valid.shape[1]
+    if kpts.shape != (B, R, 2) or kpt_valid.shape != (B, R):
+        raise ValueError("kpts must be [B,R,2] and kpt_valid [B,R]")
+    if out is None:
+        out = torch.empty((B, R, C), dtype=support.dtype, device=support.device)
+    _dev(out, "out", support.dtype)
+    if out.shape != (B, R, C):
+        raise ValueError("out must be [B,R,C]")
+    _check(lib.gkd_vkp_pool(_ptr(support), _ptr(kpts), _ptr(kpt_valid), B, C, H, W, R,
+                            float(stride), float(sigma), _dtype_code(support), 0,
+                            _ptr(out), _stream(support.device)))
+    return out
+
+
+def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=None,
+                   mask_txt=None, decode: bool = True, out=None, out_decode=None):
+    """query [B,C,H,W] (f32|bf16); kern_* [B,R,C] in the query dtype with
+    mask_* [B,R] u8 (None = modality absent).
+
+    Returns heatmaps [B,R,4H,4W] f32 and, if decode, (idx [B,R] i32,
+    xy [B,R,2] f32, score [B,R] f32). Rows with no mask set are not written
+    (they keep whatever `out` held)."""
+    lib = load()
+    _dev(query, "query", ndim=4)
+    B, C, H, W = query.shape
+    R = None
+    for k, m, name in ((kern_vis, mask_vis, "vis"), (kern_txt, mask_txt, "txt")):
+        if (k is None) != (m is None):
+            raise ValueError(f"kern_{name} and mask_{name} go together")
+        if k is not None:
+            _dev(k, f"kern_{name}", query.dtype, 3)
+            _dev(m, f"mask_{name}", torch.uint8, 2)
+            if R is None:
+                R = m.shape[1]
+            if k.shape != (B, R, C) or m.shape != (B, R):
+                raise ValueError(f"kern_{name} must be [B,R,C], mask_{name} [B,R]")
+    if R is None:
+        raise ValueError("at least one prompt modality is required")
+    if out is None:
+        out = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.float32, device=query.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (B, R, 4 * H, 4 * W):
+        raise ValueError("out must be [B,R,4H,4W]")
+    idx = xy = score = None
+    if decode:
+        if out_decode is None:
+            idx = torch.empty((B, R), dtype=torch.int32, device=query.device)
+            xy = torch.empty((B, R, 2), dtype=torch.float32, device=query.device)
+            score = torch.empty((B, R), dtype=torch.float32, device=query.device)
+        else:
+            idx, xy, score = out_decode
+    _check(lib.gkd_kernel_heatmap(_ptr(query), _ptr(kern_vis), _ptr(mask_vis),
+                                  _ptr(kern_txt), _ptr(mask_txt), B, C, H, W, R,
+                                  _dtype_code(query), 0, _ptr(out), _ptr(idx), _ptr(xy),
+                                  _ptr(score), _stream(query.device)))
+    if decode:
+        return out, (idx, xy, score)
+    return out
+
+
+def peak_decode(heat: torch.Tensor, row_valid: torch.Tensor | None = None):
+    """heat [B,R,Ho,Wo] f32, row_valid [B,R] u8 or None -> (idx [B,R] i32,
+    xy [B,R,2] f32, score [B,R] f32); invalid rows get (-1, NaN, -inf)."""
+    lib = load()
+    _dev(heat, "heat", torch.float32, 4)
+    B, R, Ho, Wo = heat.shape
+    if row_valid is not None:
+        _dev(row_valid, "row_valid", torch.uint8, 2)
+        if row_valid.shape != (B, R):
+            raise ValueError("row_valid must be [B,R]")
+    idx = torch.empty((B, R), dtype=torch.int32, device=heat.device)
+    xy = torch.empty((B, R, 2), dtype=torch.float32, device=heat.device)
+    score = torch.empty((B, R), dtype=torch.float32, device=heat.device)
+    _check(lib.gkd_peak_decode(_ptr(heat), _ptr(row_valid), B, R, Ho, Wo, 0, _ptr(idx),
+                               _ptr(xy), _ptr(score), _stream(heat.device)))
+    return idx, xy, score

@@ -1,0 +1,180 @@
+// api.hip - the C ABI of libgkdhead: argument validation, status codes,
+// thread-local error text, and dispatch to the kernel launchers.
+//
+// Every check runs before the first HIP call, so an invalid call launches
+// nothing, writes nothing and does not even touch the HIP runtime.
+#include "gkdhead.h"
+#include "launch.hpp"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gkd_status fail(gkd_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gkd_status ok() {
+  g_err[0] = '\0';
+  return GKD_OK;
+}
+
+constexpr long long kMaxElems = 0x7fffffffLL;  // element counts < 2^31
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+gkd_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(GKD_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gkd_abi_version(void) { return GKD_ABI_VERSION; }
+
+const char* gkd_status_string(int status) {
+  switch (status) {
+    case GKD_OK: return "GKD_OK";
+    case GKD_ERR_NULL: return "GKD_ERR_NULL";
+    case GKD_ERR_SHAPE: return "GKD_ERR_SHAPE";
+    case GKD_ERR_DTYPE: return "GKD_ERR_DTYPE";
+    case GKD_ERR_VALUE: return "GKD_ERR_VALUE";
+    case GKD_ERR_UNSUPPORTED: return "GKD_ERR_UNSUPPORTED";
+    case GKD_ERR_HIP: return "GKD_ERR_HIP";
+    case GKD_ERR_ALIGN: return "GKD_ERR_ALIGN";
+    default: return "GKD_ERR_UNKNOWN";
+  }
+}
+
+const char* gkd_last_error(void) { return g_err; }
+
+gkd_status gkd_vkp_pool(const void* support, const float* kpts_px, const uint8_t* kpt_valid,
+                        int B, int C, int H, int W, int R, float stride_px, float sigma_px,
+                        gkd_dtype dtype, uint32_t flags, void* protos, hipStream_t stream) {
+  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_vkp_pool: flags must be 0");
+  if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
+    return fail(GKD_ERR_DTYPE, "gkd_vkp_pool: unknown dtype %d", (int)dtype);
+  if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1)
+    return fail(GKD_ERR_SHAPE, "gkd_vkp_pool: bad shape B=%d C=%d H=%d W=%d R=%d", B, C, H, W, R);
+  if (!std::isfinite(stride_px) || !(stride_px > 0.f))
+    return fail(GKD_ERR_VALUE, "gkd_vkp_pool: stride_px must be finite and > 0");
+  if (!std::isfinite(sigma_px) || !(sigma_px > 0.f))
+    return fail(GKD_ERR_VALUE, "gkd_vkp_pool: sigma_px must be finite and > 0");
+  if ((long long)C * H * W > kMaxElems || (long long)B * C * H * W > kMaxElems ||
+      (long long)B * R * C > kMaxElems || (long long)B * R * 2 > kMaxElems)
+    return fail(GKD_ERR_SHAPE, "gkd_vkp_pool: an element count reaches 2^31");
+  if (B == 0 || R == 0) return ok();
+  if (!support || !kpts_px || !kpt_valid || !protos)
+    return fail(GKD_ERR_NULL, "gkd_vkp_pool: NULL pointer argument");
+  if (!aligned16(support) || !aligned16(protos) || !aligned4(kpts_px))
+    return fail(GKD_ERR_ALIGN, "gkd_vkp_pool: support/protos need 16-byte, kpts 4-byte alignment");
+  gkd::VkpArgs a;
+  a.support = support;
+  a.kpts = kpts_px;
+  a.valid = kpt_valid;
+  a.B = B;
+  a.C = C;
+  a.H = H;
+  a.W = W;
+  a.R = R;
+  a.stride = stride_px;
+  a.sigma = sigma_px;
+  a.bf16 = dtype == GKD_DTYPE_BF16;
+  a.protos = protos;
+  return hip_status(gkd::launch_vkp(a, stream), "gkd_vkp_pool");
+}
+
+gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uint8_t* mask_vis,
+                              const void* kern_txt, const uint8_t* mask_txt, int B, int C,
+                              int H, int W, int R, gkd_dtype dtype, uint32_t flags,
+                              float* heatmaps, int32_t* peak_idx, float* peak_xy,
+                              float* peak_score, hipStream_t stream) {
+  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: flags must be 0");
+  if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
+    return fail(GKD_ERR_DTYPE, "gkd_kernel_heatmap: unknown dtype %d", (int)dtype);
+  if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1)
+    return fail(GKD_ERR_SHAPE, "gkd_kernel_heatmap: bad shape B=%d C=%d H=%d W=%d R=%d", B, C,
+                H, W, R);
+  if ((long long)B * C * H * W > kMaxElems || (long long)B * R * C > kMaxElems ||
+      (long long)B * R * 16 * H * W > kMaxElems || (long long)B * R * 2 > kMaxElems)
+    return fail(GKD_ERR_SHAPE, "gkd_kernel_heatmap: an element count reaches 2^31");
+  if ((long long)H * W > gkd::kHeatmapMaxS)
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: H*W=%lld beyond the maximum %d",
+                (long long)H * W, gkd::kHeatmapMaxS);
+  if (gkd::plan_heatmap(C, H * W, dtype == GKD_DTYPE_BF16).rows_per_item < 1)
+    return fail(GKD_ERR_UNSUPPORTED,
+                "gkd_kernel_heatmap: C=%d with H*W=%d does not fit the kernel's LDS budget", C,
+                H * W);
+  if (B == 0 || R == 0) return ok();
+  if (!query || !heatmaps) return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: NULL query/heatmaps");
+  if ((kern_vis == nullptr) != (mask_vis == nullptr) ||
+      (kern_txt == nullptr) != (mask_txt == nullptr))
+    return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: a kernel/mask pair is half NULL");
+  if (!kern_vis && !kern_txt)
+    return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: no prompt modality given");
+  const int ndec = (peak_idx != nullptr) + (peak_xy != nullptr) + (peak_score != nullptr);
+  if (ndec != 0 && ndec != 3)
+    return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: decode outputs must be all NULL or all set");
+  if (!aligned16(query) || !aligned16(heatmaps) || (kern_vis && !aligned16(kern_vis)) ||
+      (kern_txt && !aligned16(kern_txt)))
+    return fail(GKD_ERR_ALIGN, "gkd_kernel_heatmap: query/kernels/heatmaps need 16-byte alignment");
+  if (ndec && (!aligned4(peak_idx) || !aligned4(peak_xy) || !aligned4(peak_score)))
+    return fail(GKD_ERR_ALIGN, "gkd_kernel_heatmap: decode outputs need 4-byte alignment");
+  gkd::HeatmapArgs a;
+  a.query = query;
+  a.kv = kern_vis;
+  a.mv = mask_vis;
+  a.kt = kern_txt;
+  a.mt = mask_txt;
+  a.B = B;
+  a.C = C;
+  a.H = H;
+  a.W = W;
+  a.R = R;
+  a.bf16 = dtype == GKD_DTYPE_BF16;
+  a.heat = heatmaps;
+  a.idx = peak_idx;
+  a.xy = peak_xy;
+  a.score = peak_score;
+  return hip_status(gkd::launch_heatmap(a, stream), "gkd_kernel_heatmap");
+}
+
+gkd_status gkd_peak_decode(const float* heatmaps, const uint8_t* row_valid, int B, int R, int Ho,
+                           int Wo, uint32_t flags, int32_t* peak_idx, float* peak_xy,
+                           float* peak_score, hipStream_t stream) {
+  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_peak_decode: flags must be 0");
+  if (B < 0 || R < 0 || Ho < 1 || Wo < 1)
+    return fail(GKD_ERR_SHAPE, "gkd_peak_decode: bad shape B=%d R=%d Ho=%d Wo=%d", B, R, Ho, Wo);
+  if ((long long)B * R * Ho * Wo > kMaxElems || (long long)B * R * 2 > kMaxElems)
+    return fail(GKD_ERR_SHAPE, "gkd_peak_decode: an element count reaches 2^31");
+  if (B == 0 || R == 0) return ok();
+  if (!heatmaps || !peak_idx || !peak_xy || !peak_score)
+    return fail(GKD_ERR_NULL, "gkd_peak_decode: NULL pointer argument");
+  if (!aligned16(heatmaps) || !aligned4(peak_idx) || !aligned4(peak_xy) || !aligned4(peak_score))
+    return fail(GKD_ERR_ALIGN, "gkd_peak_decode: heatmaps need 16-byte, outputs 4-byte alignment");
+  gkd::DecodeArgs a;
+  a.heat = heatmaps;
+  a.valid = row_valid;
+  a.B = B;
+  a.R = R;
+  a.Ho = Ho;
+  a.Wo = Wo;
+  a.idx = peak_idx;
+  a.xy = peak_xy;
+  a.score = peak_score;
+  return hip_status(gkd::launch_decode(a, stream), "gkd_peak_decode");
+}
+
+}  // extern "C"

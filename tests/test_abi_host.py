@@ -1,0 +1,182 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every gkd_* entry point declared in
+include/gkdhead.h, and reject each invalid argument with its documented
+status before touching the HIP runtime. Every call here is invalid (or an
+empty batch), so nothing is ever launched; the fake device pointers are
+never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, DTYPE, VALUE, UNSUP, HIP, ALIGN = range(8)
+A = 0x10000          # a 16-byte aligned fake device address (never read)
+A2 = 0x20000
+A3 = 0x30000
+MIS = 0x10002        # misaligned
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0   # counts without initialising HIP
+
+
+# The fake addresses above must never reach a kernel: every call in this
+# module is invalid or empty by construction, and the module does not run
+# where a GPU is visible at all.
+pytestmark = pytest.mark.skipif(_gpu_visible(),
+                                reason="host-only validation tests (fake device pointers)")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import prompt_conditioned_keypoint_amd as gkd
+    return gkd.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gkdhead.h")).read()
+    return sorted(set(re.findall(r"\b(gkd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gkd_vkp_pool", "gkd_kernel_heatmap", "gkd_peak_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gkd_abi_version() == 1
+    for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
+                                 "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
+                                 "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
+                                 "GKD_ERR_ALIGN"]):
+        assert lib.gkd_status_string(code).decode() == name
+    assert lib.gkd_status_string(99).decode() == "GKD_ERR_UNKNOWN"
+    assert lib.gkd_status_string(-1) is not None
+
+
+def hm(lib, query=A, kv=A2, mv=A3, kt=None, mt=None, B=2, C=64, H=24, W=24, R=80,
+       dtype=1, flags=0, heat=A, idx=None, xy=None, score=None):
+    return lib.gkd_kernel_heatmap(query, kv, mv, kt, mt, B, C, H, W, R, dtype, flags,
+                                  heat, idx, xy, score, None)
+
+
+def vk(lib, support=A, kpts=A2, valid=A3, B=2, C=64, H=24, W=24, R=80, stride=16.0,
+       sigma=14.0, dtype=1, flags=0, protos=A):
+    return lib.gkd_vkp_pool(support, kpts, valid, B, C, H, W, R, stride, sigma, dtype,
+                            flags, protos, None)
+
+
+def dec(lib, heat=A, valid=None, B=2, R=80, Ho=96, Wo=96, flags=0, idx=A, xy=A2,
+        score=A3):
+    return lib.gkd_peak_decode(heat, valid, B, R, Ho, Wo, flags, idx, xy, score, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=1), UNSUP),
+    (dict(dtype=2), DTYPE),
+    (dict(dtype=-1), DTYPE),
+    (dict(B=-1), SHAPE),
+    (dict(R=-3), SHAPE),
+    (dict(C=0), SHAPE),
+    (dict(H=0), SHAPE),
+    (dict(W=-2), SHAPE),
+    (dict(B=1 << 20, C=1024), SHAPE),          # B*C*H*W >= 2^31
+    (dict(B=1000, R=80, H=48, W=48), SHAPE),   # B*R*16*H*W >= 2^31
+    (dict(H=49, W=48), UNSUP),                 # H*W beyond the kernel's limit
+    (dict(C=4096), UNSUP),                     # kernel rows do not fit LDS
+    (dict(C=1500, dtype=0), UNSUP),
+    (dict(query=None), NULL),
+    (dict(heat=None), NULL),
+    (dict(mv=None), NULL),                     # half a kernel/mask pair
+    (dict(kt=A2), NULL),
+    (dict(kv=None, mv=None), NULL),            # no modality at all
+    (dict(idx=A), NULL),                       # decode outputs half set
+    (dict(idx=A, xy=A, score=None), NULL),
+    (dict(query=MIS), ALIGN),
+    (dict(heat=MIS), ALIGN),
+    (dict(kv=MIS), ALIGN),
+    (dict(idx=A + 2, xy=A, score=A), ALIGN),
+])
+def test_kernel_heatmap_rejects(lib, kw, status):
+    assert hm(lib, **kw) == status
+    assert lib.gkd_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(R=0), dict(B=0, query=None, heat=None)])
+def test_kernel_heatmap_empty_batch_is_ok(lib, kw):
+    assert hm(lib, **kw) == OK
+    assert lib.gkd_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=7), UNSUP),
+    (dict(dtype=5), DTYPE),
+    (dict(C=0), SHAPE),
+    (dict(B=-1), SHAPE),
+    (dict(stride=0.0), VALUE),
+    (dict(stride=float("inf")), VALUE),
+    (dict(sigma=-1.0), VALUE),
+    (dict(sigma=float("nan")), VALUE),
+    (dict(support=None), NULL),
+    (dict(kpts=None), NULL),
+    (dict(valid=None), NULL),
+    (dict(protos=None), NULL),
+    (dict(support=MIS), ALIGN),
+    (dict(protos=MIS), ALIGN),
+    (dict(kpts=A + 2), ALIGN),
+    (dict(B=1 << 16, R=1 << 16), SHAPE),
+])
+def test_vkp_pool_rejects(lib, kw, status):
+    assert vk(lib, **kw) == status
+
+
+def test_vkp_pool_empty_batch_is_ok(lib):
+    assert vk(lib, B=0, support=None, kpts=None, valid=None, protos=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=1), UNSUP),
+    (dict(Ho=0), SHAPE),
+    (dict(R=-1), SHAPE),
+    (dict(B=1 << 16, R=1 << 8), SHAPE),
+    (dict(heat=None), NULL),
+    (dict(idx=None), NULL),
+    (dict(heat=MIS), ALIGN),
+    (dict(xy=A2 + 1), ALIGN),
+])
+def test_peak_decode_rejects(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_peak_decode_empty_batch_is_ok(lib):
+    assert dec(lib, R=0, heat=None) == OK
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    assert hm(lib, flags=1) == UNSUP
+    seen = {}
+
+    def other():
+        seen["text"] = lib.gkd_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["text"] == ""
+    assert "flags" in lib.gkd_last_error().decode()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import prompt_conditioned_keypoint_amd.binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        b.load()
