@@ -9,7 +9,7 @@ import torch
 
 import gkdsynth
 from parity_util import (check_decode, check_heatmaps, check_protos, dev_tensor,
-                         feat_dtype)
+                         feat_dtype, floors_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -145,10 +145,11 @@ def test_kernel_heatmap_parity(gkd, ora, name, kw, nsample):
     valid = valid_rows(d)
     g = heat.cpu().numpy()
     oh = oracle_heat(ora, d, protos, crops)
-    check_heatmaps(g[crops], oh, valid[crops], d["dtype"])
+    fl = floors_of(d["query"][crops])
+    check_heatmaps(g[crops], oh, valid[crops], d["dtype"], fl)
     n_exact, n_near = check_decode((idx.cpu().numpy()[crops], xy.cpu().numpy()[crops],
                                     score.cpu().numpy()[crops]), oh, valid[crops],
-                                   d["dtype"])
+                                   d["dtype"], floors=fl)
     assert n_exact > 0
     # rows with no prompt: heatmap untouched, decode sentinel
     gi = heat.view(torch.int32).cpu().numpy()
@@ -212,14 +213,15 @@ def test_chain_vkp_heatmap_decode(gkd, ora):
     oh = oracle_heat(ora, d, o_protos, crops)
     valid = valid_rows(d)[crops]
     g = heat.cpu().numpy()[crops]
-    check_heatmaps(g, oh, valid, "bf16")
+    fl = floors_of(d["query"][crops])
+    check_heatmaps(g, oh, valid, "bf16", fl)
     # prototypes may differ by one bf16 ulp, so the argmax is held to the
     # gap the heatmap error allows
     err = max(np.abs(g[b, r] - oh[b, r]).max() for b in range(len(crops))
               for r in range(d["R"]) if valid[b, r])
     check_decode((idx.cpu().numpy()[crops], xy.cpu().numpy()[crops],
                   score.cpu().numpy()[crops]), oh, valid, "bf16",
-                 gap_tol=max(1e-3, 4 * err))
+                 gap_tol=max(1e-3, 4 * err), floors=fl)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -249,8 +251,10 @@ def test_ragged_shapes(gkd, ora, dtype, shape):
     torch.cuda.synchronize()
     oh = ora.kernel_heatmap(q, kv, mv, kt, mt)
     valid = ((mv | mt) > 0).astype(np.uint8)
-    check_heatmaps(heat.cpu().numpy(), oh, valid, dtype)
-    check_decode((idx.cpu().numpy(), xy.cpu().numpy(), score.cpu().numpy()), oh, valid, dtype)
+    fl = floors_of(q)
+    check_heatmaps(heat.cpu().numpy(), oh, valid, dtype, fl)
+    check_decode((idx.cpu().numpy(), xy.cpu().numpy(), score.cpu().numpy()), oh, valid, dtype,
+                 floors=fl)
     assert np.all(heat.view(torch.int32).cpu().numpy()[valid == 0] == NAN_BITS)
     # VKP on the same shape
     kp = rng.uniform(0, [W * 16, H * 16], size=(B, R, 2)).astype(np.float32)
