@@ -134,8 +134,7 @@ GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
  *   peak_idx   [B,R]   int32     optional fused decode (see gkd_peak_decode);
  *   peak_xy    [B,R,2] float32   all three NULL = no decode, else all three
  *   peak_score [B,R]   float32   non-NULL. Rows with no mask get the sentinel.
- * Limits: C >= 1, H >= 1, W >= 1; H*W <= 2304; C <= 2304 (bf16) or
- * C <= 1152 (f32).
+ * Limits: C >= 1, H >= 1, W >= 1, H*W <= 16384 (else GKD_ERR_UNSUPPORTED).
  */
 GKD_API gkd_status gkd_kernel_heatmap(const void *query, const void *kern_vis,
                               const uint8_t *mask_vis, const void *kern_txt,

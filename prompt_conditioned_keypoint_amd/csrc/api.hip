@@ -115,8 +115,7 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
                 (long long)H * W, gkd::kHeatmapMaxS);
   if (gkd::plan_heatmap(C, H * W, dtype == GKD_DTYPE_BF16).rows_per_item < 1)
     return fail(GKD_ERR_UNSUPPORTED,
-                "gkd_kernel_heatmap: C=%d with H*W=%d does not fit the kernel's LDS budget", C,
-                H * W);
+                "gkd_kernel_heatmap: H*W=%d does not fit the kernel's LDS budget", H * W);
   if (B == 0 || R == 0) return ok();
   if (!query || !heatmaps) return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: NULL query/heatmaps");
   if ((kern_vis == nullptr) != (mask_vis == nullptr) ||

@@ -32,17 +32,40 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// One exchange step of the argmax reduction through a DPP lane pattern.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp_step(float& v, int& i) {
+  const float ov = __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
 // Wave64 (value desc, index asc) reduction; every lane gets the winner.
+// Within each 16-lane row: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// half-row mirror, row mirror (register-level lane moves, no LDS); then the
+// four row results are combined from readlane values.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_dpp_step<0xB1>(v, i);   // quad_perm(1,0,3,2)
+  argmax_dpp_step<0x4E>(v, i);   // quad_perm(2,3,0,1)
+  argmax_dpp_step<0x141>(v, i);  // row_half_mirror
+  argmax_dpp_step<0x140>(v, i);  // row_mirror
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off, kWave);
-    const int oi = __shfl_xor(i, off, kWave);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
     }
   }
+  v = bv;
+  i = bi;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -105,6 +128,33 @@ __device__ __forceinline__ void select_rows(const uint8_t* m0, const uint8_t* m1
     *n_valid = total;
     *n_sel = (blk < nb) ? hi - lo : 0;
   }
+}
+
+// ---------------------------------------------------------------------------
+// 4x bilinear expand of one low-res cell (half-pixel centres, edge clamp).
+// Output sample 4i + d reads source rows (lo, hi) with weights (wl, wh):
+//   d=0: (i-1, i) (3/8, 5/8)   d=1: (i-1, i) (1/8, 7/8)
+//   d=2: (i, i+1) (7/8, 1/8)   d=3: (i, i+1) (5/8, 3/8)
+// and at a clamped border (1, 0) on the cell itself, which reproduces the
+// border duplicates bit for bit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void bilinear_taps4(int i, int n, float (&wl)[4], float (&wh)[4]) {
+  const bool lo_ok = i > 0, hi_ok = i < n - 1;
+  wl[0] = lo_ok ? 0.375f : 1.f;  wh[0] = lo_ok ? 0.625f : 0.f;
+  wl[1] = lo_ok ? 0.125f : 1.f;  wh[1] = lo_ok ? 0.875f : 0.f;
+  wl[2] = hi_ok ? 0.875f : 1.f;  wh[2] = hi_ok ? 0.125f : 0.f;
+  wl[3] = hi_ok ? 0.625f : 1.f;  wh[3] = hi_ok ? 0.375f : 0.f;
+}
+
+// h[d] for one source row r: horizontal taps around column j.
+__device__ __forceinline__ void bilinear_hrow(const float* __restrict__ Pr, int j, int jm, int jp,
+                                     const float (&wl)[4], const float (&wh)[4],
+                                     float (&h)[4]) {
+  const float a = Pr[jm], c = Pr[j], e = Pr[jp];
+  h[0] = fmaf(wh[0], c, wl[0] * a);
+  h[1] = fmaf(wh[1], c, wl[1] * a);
+  h[2] = fmaf(wh[2], e, wl[2] * c);
+  h[3] = fmaf(wh[3], e, wl[3] * c);
 }
 
 }  // namespace gkd

@@ -40,23 +40,22 @@ struct DecodeArgs {
   float* score;
 };
 
-// Shape limits of the heatmap kernel. Its LDS holds the kernel rows of
-// both modalities for all C channels plus the fused low-res maps of at least
-// one row (aliased with the kernel rows for small maps).
-constexpr int kHeatmapMaxS = 2304;
+// Shape limits of the heatmap kernel: its LDS holds the fused low-res maps
+// of at least one row (S floats).
+constexpr int kHeatmapMaxS = 16384;
 constexpr size_t kLdsBudget = 150 * 1024;  // of 160 KiB; the rest is static
 
 struct HeatmapPlan {
-  int cp = 0;             // C rounded up to the K step
-  int ldk = 0;            // LDS row stride of the kernel tile (elements)
-  int nstw = 0;           // 64-pixel super-tiles per wave
+  int nsteps = 0;         // K steps over the channels
   int rows_per_item = 0;  // 0 = shape does not fit
-  int p_offset = 0;       // LDS byte offset of the fused maps
   size_t lds_bytes = 0;   // dynamic LDS per workgroup
 };
 HeatmapPlan plan_heatmap(int C, int S, bool bf16);
 
 hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream);
+// bf16 fast path (direct-to-LDS staging, transposing LDS reads)
+bool heatmap_lds_applicable(int C, int S, bool bf16);
+hipError_t launch_heatmap_lds(const HeatmapArgs& a, hipStream_t stream);
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

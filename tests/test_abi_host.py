@@ -90,9 +90,8 @@ def dec(lib, heat=A, valid=None, B=2, R=80, Ho=96, Wo=96, flags=0, idx=A, xy=A2,
     (dict(W=-2), SHAPE),
     (dict(B=1 << 20, C=1024), SHAPE),          # B*C*H*W >= 2^31
     (dict(B=1000, R=80, H=48, W=48), SHAPE),   # B*R*16*H*W >= 2^31
-    (dict(H=49, W=48), UNSUP),                 # H*W beyond the kernel's limit
-    (dict(C=4096), UNSUP),                     # kernel rows do not fit LDS
-    (dict(C=1500, dtype=0), UNSUP),
+    (dict(H=129, W=128, R=1), UNSUP),          # H*W beyond the kernel's limit
+    (dict(H=1, W=16385, R=1, dtype=0), UNSUP),
     (dict(query=None), NULL),
     (dict(heat=None), NULL),
     (dict(mv=None), NULL),                     # half a kernel/mask pair
