@@ -36,7 +36,10 @@ sys.path.insert(0, ROOT)
 METRIC = "heatmaps/sec (96×96, C=1024, K=80, B=256) + % of HBM roofline"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "heatmap_bf16_longtail_traffic.txt")
-HEATMAP_SRC = os.path.join(ROOT, "prompt_conditioned_keypoint_amd", "csrc", "heatmap.hip")
+CSRC = os.path.join(ROOT, "prompt_conditioned_keypoint_amd", "csrc")
+# sources of the heatmap call's kernels (the counters are void once they change)
+HEATMAP_SRCS = [os.path.join(CSRC, n) for n in
+                ("heatmap.hip", "heatmap_stream.hip", "gkd_device.hpp", "launch.hpp")]
 
 
 def log(msg):
@@ -57,9 +60,12 @@ def algorithmic_bytes(d):
     return int(heat), int(vkp), int(rv)
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -72,7 +78,7 @@ def read_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("heatmap_hip_sha256_16") != src_hash(HEATMAP_SRC):
+    if vals.get("heatmap_src_sha256_16") != src_hash(HEATMAP_SRCS):
         return None
     try:
         return int(float(vals["traffic_bytes_per_launch"]))

@@ -113,9 +113,15 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   if ((long long)H * W > gkd::kHeatmapMaxS)
     return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: H*W=%lld beyond the maximum %d",
                 (long long)H * W, gkd::kHeatmapMaxS);
-  if (gkd::plan_heatmap(C, H * W, dtype == GKD_DTYPE_BF16).rows_per_item < 1)
-    return fail(GKD_ERR_UNSUPPORTED,
-                "gkd_kernel_heatmap: H*W=%d does not fit the kernel's LDS budget", H * W);
+  {
+    const bool bf16 = dtype == GKD_DTYPE_BF16;
+    const bool fits = gkd::heatmap_stream_applicable(C, H * W, bf16)
+                          ? gkd::plan_heatmap_stream(B, C, H * W, R).ok
+                          : gkd::plan_heatmap(C, H * W, bf16).rows_per_item >= 1;
+    if (!fits)
+      return fail(GKD_ERR_UNSUPPORTED,
+                  "gkd_kernel_heatmap: H*W=%d does not fit the kernel's LDS budget", H * W);
+  }
   if (B == 0 || R == 0) return ok();
   if (!query || !heatmaps) return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: NULL query/heatmaps");
   if ((kern_vis == nullptr) != (mask_vis == nullptr) ||

@@ -454,9 +454,7 @@ HeatmapPlan plan_heatmap(int C, int S, bool bf16) {
 }
 
 hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream) {
-#ifndef GKD_NO_LDS_PATH
-  if (heatmap_lds_applicable(a.C, a.H * a.W, a.bf16)) return launch_heatmap_lds(a, stream);
-#endif
+  if (heatmap_stream_applicable(a.C, a.H * a.W, a.bf16)) return launch_heatmap_stream(a, stream);
   HmParams p;
   p.query = a.query;
   p.kv = a.kv;

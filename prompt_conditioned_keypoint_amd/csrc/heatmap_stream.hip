@@ -1,0 +1,760 @@
+// heatmap_stream.hip - gkd_kernel_heatmap for bf16 features: two launches
+// on the caller's stream, each shaped for one side of the memory system.
+//
+// The head (GKDT-L GGUF model card, section "Model": rows padded to 80
+// with masks, L2 kernel norm, 1x1 kernel conv against 4x bilinearly
+// upsampled dense features, per-row fusion of the prompt modalities,
+// argmax read out as a -1..1 keypoint plus score) is linear up to the
+// argmax, so the contraction runs at the features' own resolution and only
+// its result is expanded.
+//
+// 1. contract_kernel (HBM reads): one workgroup per (crop, pixel chunk)
+//    takes ALL valid rows of the crop (up to 80 per item, both
+//    modalities), so every feature byte crosses HBM and the CU exactly
+//    once. Feature tiles [32 channels][chunk pixels] and the rows' kernel
+//    slices stream straight into a three-stage LDS ring
+//    (global_load_lds_dwordx4); MFMA B operands come from transposing LDS
+//    reads (ds_read_b64_tr_b16), A operands from plain 16-byte LDS reads.
+//    The fused low-resolution map of a row (float32, H*W values) is parked
+//    in the first H*W floats of that row's own heatmap.
+// 2. expand_kernel (HBM writes): one wave per valid row reads its parked
+//    map into LDS, writes the 4x bilinear expansion with 16-byte
+//    non-temporal stores and reduces the first-occurrence argmax in
+//    registers. Waves are independent (no workgroup barrier), so a CU
+//    keeps many rows' stores in flight.
+// The parked maps are 1/16 of the heatmap bytes; they are read back before
+// the same wave overwrites them.
+#include "gkd_device.hpp"
+#include "launch.hpp"
+
+#include <climits>
+#include <cmath>
+
+namespace gkd {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// ---------------------------------------------------------------------------
+// contraction
+// ---------------------------------------------------------------------------
+constexpr int kCWaves = 12;
+constexpr int kCThreads = kCWaves * kWave;  // 768
+constexpr int kKS = 32;                     // channels per K step (one MFMA K)
+constexpr int kFStages = 3;                 // feature ring: loads run 2 steps ahead
+constexpr int kAStages = 5;                 // kernel-row ring: loads run 4 steps ahead
+constexpr int kGroupPx = 48;                // one wave unit: 3 N tiles of 16 pixels
+constexpr int kItemRows = 80;               // valid rows per item
+constexpr int kMaxMH = kItemRows / 16;      // M tiles per modality
+constexpr int kMaxDualUnits = 3;            // wave units with both modalities (acc budget)
+constexpr int kMaxDma = 5;                  // direct-to-LDS loads per wave per stage
+constexpr int kRowSlots = 5;                // kernel row in LDS: 4 x 16 B + 1 pad slot
+constexpr int kVis = 1, kTxt = 2;
+
+struct ContractParams {
+  const uint16_t* query;
+  const uint16_t* kv;
+  const uint8_t* mv;
+  const uint16_t* kt;
+  const uint8_t* mt;
+  int B, C, H, W, R, S;
+  int ng;        // wave N groups per chunk (divides 12)
+  int chunk_px;  // ng * 48
+  int nchunks, rblocks, items_per_crop, nsteps;
+  int halves;       // 2: a dual-prompt block of more than 48 rows takes two passes
+  int lds_bytes;    // dynamic LDS of the workgroup
+  float* heat;
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 layout:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// Workgroup barrier without a memory fence (a fence would also drain the
+// direct-to-LDS loads in flight). This wave's own LDS accesses are
+// completed first; its direct-to-LDS loads are the caller's business.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Each K step stages [32 feature rows x chunk] in the feature ring and
+// [the item's kernel rows x 32 channels] in the kernel-row ring, both as
+// whole 1 KiB blocks (one load instruction: 64 lanes x 16 B, lane order).
+// Feature block q goes to wave q % 12; kernel-row blocks continue the same
+// round robin after the feature blocks, so no wave issues more than
+// ceil(blocks / 12) loads per step. Per lane and instruction: a source kind
+// (feature map, visual or text kernel rows, or a stand-in that is never
+// read) and an element offset.
+enum : uint32_t { kSrcF = 0, kSrcV = 1, kSrcT = 2, kSrcJunk = 3 };
+struct DmaPlan {
+  uint32_t off[kMaxDma];
+  uint32_t kinds;  // 2 bits per instruction
+  int nf;          // feature loads of this wave per step (instructions 0 .. nf-1)
+  int na;          // kernel-row loads per step (instructions nf .. nf+na-1)
+  int qa0;         // first kernel-row block of this wave
+};
+struct DmaBases {
+  const uint16_t* F;   // the crop's feature map
+  const uint16_t* kv;  // the crop's visual kernel rows (or F)
+  const uint16_t* kt;  // the crop's text kernel rows (or F)
+  size_t fstep;        // feature elements per K step: 32 * S
+};
+
+__device__ __forceinline__ uint64_t dma_source(const DmaPlan& pl, const DmaBases& bs, int i,
+                                               int step) {
+  const uint64_t f = (uint64_t)(bs.F + (size_t)step * bs.fstep);
+  const uint64_t v = (uint64_t)(bs.kv + (size_t)step * kKS);
+  const uint64_t t = (uint64_t)(bs.kt + (size_t)step * kKS);
+  const uint64_t j = (uint64_t)bs.F;
+  const uint32_t kind = (pl.kinds >> (2 * i)) & 3u;
+  // branch-free per-lane choice of the source
+  const uint64_t lo = (kind & 1u) ? v : f;
+  const uint64_t hi = (kind & 1u) ? j : t;
+  return ((kind & 2u) ? hi : lo) + 2ull * pl.off[i];
+}
+
+// feature blocks of one step into feature slot fs
+__device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases& bs,
+                                               unsigned char* fs, int wave, int step) {
+#pragma unroll
+  for (int i = 0; i < kMaxDma; ++i)
+    if (i < pl.nf)
+      __builtin_amdgcn_global_load_lds((glb_void*)dma_source(pl, bs, i, step),
+                                       (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024),
+                                       16, 0, 0);
+}
+
+// kernel-row blocks of one step into kernel-row slot as
+__device__ __forceinline__ void issue_rows(const DmaPlan& pl, const DmaBases& bs,
+                                           unsigned char* as, int step) {
+#pragma unroll
+  for (int i = 0; i < kMaxDma; ++i)
+    if (i >= pl.nf && i < pl.nf + pl.na)
+      __builtin_amdgcn_global_load_lds(
+          (glb_void*)dma_source(pl, bs, i, step),
+          (lds_void*)(as + (size_t)(pl.qa0 + kCWaves * (i - pl.nf)) * 1024), 16, 0, 0);
+}
+
+struct ItemShape {
+  int ng;      // wave N groups of the item's chunk
+  int chunk_px;
+  int rs;      // 16-byte slots per LDS feature row: chunk_px / 8 + 1 (one pad)
+  int nsel;    // valid rows of the item
+  int MH;      // M tiles per modality
+  int nmod;    // modalities present (1 or 2)
+  int arows;   // kernel rows staged per step: nmod * MH * 16
+  int fbytes;  // feature slot (whole 1 KiB blocks)
+  int abytes;  // kernel-row slot (whole 1 KiB blocks)
+  int px0;     // first pixel of the chunk
+  bool has_v;
+};
+
+// K loop, row norms and epilogue for one item. MODE: modalities present;
+// UPW: wave units (one M tile x one 48-pixel group) a wave may own.
+template <int MODE, int UPW>
+__device__ __forceinline__ void contract_item(const ContractParams& p, unsigned char* lds,
+                                              const DmaPlan& pl, const DmaBases& bs,
+                                              const ItemShape& it, int b, int wave, int lane,
+                                              const int* s_rows, const uint8_t* s_mv,
+                                              const uint8_t* s_mt, float (*s_w)[kItemRows]) {
+  constexpr int NM = (MODE == (kVis | kTxt)) ? 2 : 1;
+  const int tid = wave * kWave + lane;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int gw = wave % it.ng;           // this wave's pixel group
+  const int h0 = wave / it.ng;           // first M tile
+  const int hstep = kCWaves / it.ng;
+  const int gpx = gw * kGroupPx;         // group start within the chunk
+  const int row_bytes = it.rs * 16;
+  const int arow0 = it.MH * 16;          // kernel rows per modality in LDS
+
+  bool on[NM][UPW];
+#pragma unroll
+  for (int u = 0; u < UPW; ++u) {
+    const int slot = 16 * (h0 + u * hstep) + n16;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const bool vis = (MODE == kVis) || (MODE == (kVis | kTxt) && m == 0);
+      on[m][u] = slot < it.nsel && (vis ? s_mv[slot] : s_mt[slot]);
+    }
+  }
+  f32x4 acc[UPW][NM][3];
+#pragma unroll
+  for (int u = 0; u < UPW; ++u)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) acc[u][m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // row norms: thread 4 a + c sums the squares of 16-byte column c of
+  // staged kernel row a, step by step
+  const bool norm_thread = tid < 4 * it.arows;
+  const int nrow = tid >> 2, ncol = tid & 3;
+  float ss = 0.f;
+
+  unsigned char* const aring = lds + (size_t)kFStages * it.fbytes;
+  for (int k = 0; k < p.nsteps; ++k) {
+    if (k > 0) {
+      // features of step k and kernel rows of step k (issued earlier) have
+      // landed for this wave once at most these younger loads remain:
+      // rows k+2, features k+1, rows k+3 (those that were issued)
+      const int younger = (k + 1 < p.nsteps ? pl.nf : 0) + (k + 2 < p.nsteps ? pl.na : 0) +
+                          (k + 3 < p.nsteps ? pl.na : 0);
+      wait_vmcnt_upto(younger);
+    }
+    lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
+    if (k + 2 < p.nsteps)
+      issue_features(pl, bs, lds + (size_t)((k + 2) % kFStages) * it.fbytes, wave, k + 2);
+    if (k + 4 < p.nsteps)
+      issue_rows(pl, bs, aring + (size_t)((k + 4) % kAStages) * it.abytes, k + 4);
+
+    const unsigned char* sb = lds + (size_t)(k % kFStages) * it.fbytes;
+    const unsigned char* sa = aring + (size_t)(k % kAStages) * it.abytes;
+    // B: lane (n16, g4) of N tile t receives channels 8 g4 .. 8 g4 + 7 of
+    // pixel gpx + 16 t + n16 from two transposing 8-byte reads (rows
+    // 8 g4 + n16/4 and +4, columns 4 (n16 % 4) .. +3 of the tile)
+    const int r0 = 8 * g4 + (n16 >> 2);
+    const uint32_t lo_addr =
+        (uint32_t)(uintptr_t)(lds_void*)(sb + r0 * row_bytes + (gpx + 4 * (n16 & 3)) * 2);
+    const uint32_t hi_addr = lo_addr + 4 * row_bytes;
+    u32x2 blo[3], bhi[3];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %6\n"
+        "ds_read_b64_tr_b16 %1, %6 offset:32\n"
+        "ds_read_b64_tr_b16 %2, %6 offset:64\n"
+        "ds_read_b64_tr_b16 %3, %7\n"
+        "ds_read_b64_tr_b16 %4, %7 offset:32\n"
+        "ds_read_b64_tr_b16 %5, %7 offset:64\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(blo[0]), "=&v"(blo[1]), "=&v"(blo[2]), "=&v"(bhi[0]), "=&v"(bhi[1]),
+          "=&v"(bhi[2])
+        : "v"(lo_addr), "v"(hi_addr)
+        : "memory");
+    bf16x8 bv[3];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      bv[t] = __builtin_bit_cast(bf16x8, u32x4{blo[t].x, blo[t].y, bhi[t].x, bhi[t].y});
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+      const int h = h0 + u * hstep;
+      if (h >= it.MH) break;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const int ar = m * arow0 + 16 * h + n16;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sa + ar * (kRowSlots * 16) + 16 * g4);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, on[m][u] ? v : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          acc[u][m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv[t], acc[u][m][t], 0, 0, 0);
+      }
+    }
+    if (norm_thread) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sa + nrow * (kRowSlots * 16) + 16 * ncol);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const float lo = __uint_as_float(v[d] << 16), hi = __uint_as_float(v[d] & 0xffff0000u);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+  }
+  // fusion weights mask / (n ||k||) from the norms
+  ss += __shfl_xor(ss, 1, kWave);
+  ss += __shfl_xor(ss, 2, kWave);
+  if (norm_thread && ncol == 0) {
+    const int mi = nrow / arow0, slot = nrow - mi * arow0;
+    const int mod = (it.has_v && mi == 0) ? 0 : 1;
+    if (slot < it.nsel) {
+      const bool on_row = mod == 0 ? s_mv[slot] : s_mt[slot];
+      float w = 0.f;
+      if (on_row) {
+        const float n = (float)((int)s_mv[slot] + (int)s_mt[slot]);
+        w = 1.f / (fmaxf(sqrtf(ss), 1e-12f) * n);
+      }
+      s_w[mod][slot] = w;
+    }
+  }
+  lds_barrier();  // the ring is free; the weights are visible
+
+  // fused low-res maps -> LDS rows (passes of up to rows_per_pass) -> the
+  // first H*W floats of each row's heatmap with 16-byte stores. Lane
+  // (n16, g4) holds rows 4 g4 + i of each M tile at pixel 16 t + n16.
+  float* Pl = reinterpret_cast<float*>(lds);
+  const int pitch = it.chunk_px + 4;
+  const int rows_per_pass = p.lds_bytes / (pitch * 4);
+  const int q4 = it.chunk_px / 4;
+  const size_t hw_out = (size_t)16 * p.S;
+  for (int base = 0; base < it.nsel; base += rows_per_pass) {
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+      const int h = h0 + u * hstep;
+      if (h >= it.MH) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int slot = 16 * h + 4 * g4 + i;
+        if (slot < base || slot >= base + rows_per_pass || slot >= it.nsel) continue;
+        float* dst = Pl + (slot - base) * pitch + gpx + n16;
+        if constexpr (NM == 2) {
+          const float wv = s_w[0][slot], wt = s_w[1][slot];
+#pragma unroll
+          for (int t = 0; t < 3; ++t) dst[16 * t] = fmaf(wt, acc[u][1][t][i], wv * acc[u][0][t][i]);
+        } else {
+          const float w = s_w[MODE == kVis ? 0 : 1][slot];
+#pragma unroll
+          for (int t = 0; t < 3; ++t) dst[16 * t] = w * acc[u][0][t][i];
+        }
+      }
+    }
+    lds_barrier();
+    const int nrows = min(rows_per_pass, it.nsel - base);
+    for (int e = tid; e < nrows * q4; e += kCThreads) {
+      const int r = e / q4, c4 = e - r * q4;
+      const int px = it.px0 + 4 * c4;
+      if (px < p.S) {
+        const f32x4 val = *reinterpret_cast<const f32x4*>(Pl + r * pitch + 4 * c4);
+        *reinterpret_cast<f32x4*>(p.heat + ((size_t)b * p.R + s_rows[base + r]) * hw_out + px) =
+            val;
+      }
+    }
+    lds_barrier();
+  }
+}
+
+template <int MODE, int MAXU>
+__device__ __forceinline__ void contract_dispatch(int upw, const ContractParams& p,
+                                                  unsigned char* lds, const DmaPlan& pl,
+                                                  const DmaBases& bs, const ItemShape& it, int b,
+                                                  int wave, int lane, const int* s_rows,
+                                                  const uint8_t* s_mv, const uint8_t* s_mt,
+                                                  float (*s_w)[kItemRows]) {
+#define GKD_CONTRACT(U) \
+  contract_item<MODE, (U < MAXU ? U : MAXU)>(p, lds, pl, bs, it, b, wave, lane, s_rows, s_mv, \
+                                             s_mt, s_w)
+  switch (upw) {
+    case 1: GKD_CONTRACT(1); break;
+    case 2: GKD_CONTRACT(2); break;
+    case 3: GKD_CONTRACT(3); break;
+    case 4: GKD_CONTRACT(4); break;
+    default: GKD_CONTRACT(5); break;
+  }
+#undef GKD_CONTRACT
+}
+
+__global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  __shared__ int s_rows[kItemRows];
+  __shared__ uint8_t s_mv[kItemRows], s_mt[kItemRows];
+  __shared__ int s_nvalid, s_nsel;
+  __shared__ float s_w[2][kItemRows];  // fusion weights: mask / (n ||k||)
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ItemCoord ic = xcd_item(blockIdx.x, p.items_per_crop);
+  const int b = ic.crop;
+  if (b >= p.B) return;
+  const int chunk = ic.item % p.nchunks, rblk = ic.item / p.nchunks;
+  const uint8_t* mv = p.mv ? p.mv + (size_t)b * p.R : nullptr;
+  const uint8_t* mt = p.mt ? p.mt + (size_t)b * p.R : nullptr;
+
+  if (wave == 0)
+    select_rows(mv, mt, p.R, lane, rblk, kItemRows, s_rows, s_mv, s_mt, &s_nvalid, &s_nsel);
+  __syncthreads();
+  ItemShape it;
+  it.nsel = s_nsel;
+  if (it.nsel == 0) return;
+  bool has_v = false, has_t = false;
+  int first_v = 0, first_t = 0;
+  for (int s = it.nsel - 1; s >= 0; --s) {
+    if (s_mv[s]) { has_v = true; first_v = s; }
+    if (s_mt[s]) { has_t = true; first_t = s; }
+  }
+  it.has_v = has_v;
+  it.MH = (it.nsel + 15) / 16;
+  it.nmod = (int)has_v + (int)has_t;
+  it.arows = it.nmod * it.MH * 16;
+  // both modalities over more than three M tiles would not fit the
+  // accumulators: such a block takes its chunk in two halves, one after the
+  // other (the features are still read once, the kernel rows twice). The
+  // grid holds no empty workgroups: an idle one still occupies a CU's LDS
+  // until dispatch moves on.
+  const bool split = p.halves == 2 && it.nmod == 2 && it.MH > kMaxDualUnits;
+  it.ng = split ? p.ng / 2 : p.ng;
+  it.chunk_px = it.ng * kGroupPx;
+  it.rs = it.chunk_px / 8 + 1;
+#pragma nounroll
+  for (int half = 0; half < (split ? 2 : 1); ++half) {
+  // per-pass inputs are opaque, so nothing lane-dependent from one pass is
+  // kept alive for the next
+  int lane_p = lane;
+  asm volatile("" : "+v"(lane_p));
+  it.px0 = chunk * p.chunk_px + half * it.chunk_px;
+  const int nF = kKS * it.rs;                   // feature slots of a step
+  const int nfi = (nF + kWave - 1) / kWave;     // feature blocks
+  const int nA = it.arows * kRowSlots;          // kernel-row slots of a step
+  const int nai = (nA + kWave - 1) / kWave;     // kernel-row blocks
+  it.fbytes = nfi * 1024;
+  it.abytes = nai * 1024;
+
+  DmaBases bs;
+  bs.F = p.query + (size_t)b * p.C * p.S;
+  bs.fstep = (size_t)kKS * p.S;
+  bs.kv = has_v ? p.kv + (size_t)b * p.R * p.C : bs.F;
+  bs.kt = has_t ? p.kt + (size_t)b * p.R * p.C : bs.F;
+
+  // ---- DMA plan. Feature slot u < nF: feature row r = u / rs (channel),
+  // 16-byte column u % rs (the last one pads the row); past the map: the
+  // row's start. Kernel-row slot v < nA: kernel row (modality index,
+  // slot) = v / 5, 16-byte column v % 5 (the fifth pads); masked or empty
+  // slots load the modality's first valid row and are zeroed before the
+  // MFMA. Everything else is a stand-in that is never read.
+  DmaPlan pl;
+  pl.nf = wave < nfi ? (nfi - wave + kCWaves - 1) / kCWaves : 0;
+  pl.qa0 = (wave - nfi % kCWaves + kCWaves) % kCWaves;
+  pl.na = pl.qa0 < nai ? (nai - pl.qa0 + kCWaves - 1) / kCWaves : 0;
+  pl.kinds = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxDma; ++i) {
+    uint32_t kind = kSrcJunk, off = 0;
+    if (i < pl.nf) {
+      const int u = (wave + kCWaves * i) * kWave + lane_p;
+      if (u < nF) {
+        const int r = u / it.rs, cc = u - r * it.rs;
+        const int px = it.px0 + 8 * cc;
+        kind = kSrcF;
+        off = (uint32_t)(r * p.S + ((cc < it.rs - 1 && px < p.S) ? px : 0));
+      }
+    } else if (i < pl.nf + pl.na) {
+      const int v = (pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p;
+      if (v < nA) {
+        const int ar = v / kRowSlots, ac = v - ar * kRowSlots;
+        const int mi = ar / (it.MH * 16), slot = ar - mi * (it.MH * 16);
+        const bool vis = has_v && mi == 0;
+        const bool on = slot < it.nsel && (vis ? s_mv[slot] : s_mt[slot]);
+        const int use = on ? slot : (vis ? first_v : first_t);
+        kind = vis ? kSrcV : kSrcT;
+        off = (uint32_t)s_rows[use] * (uint32_t)p.C + (ac < 4 ? 8 * ac : 0);
+      }
+    }
+    pl.off[i] = off;
+    pl.kinds |= kind << (2 * i);
+  }
+  unsigned char* const aring = lds + (size_t)kFStages * it.fbytes;
+  issue_features(pl, bs, lds, wave, 0);
+  if (p.nsteps > 1) issue_features(pl, bs, lds + it.fbytes, wave, 1);
+  for (int st = 0; st < kAStages - 1 && st < p.nsteps; ++st)
+    issue_rows(pl, bs, aring + (size_t)st * it.abytes, st);
+  wait_vmcnt<0>();  // the prologue steps
+
+  const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
+  if (has_v && has_t)
+    contract_dispatch<kVis | kTxt, kMaxDualUnits>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows,
+                                                  s_mv, s_mt, s_w);
+  else if (has_v)
+    contract_dispatch<kVis, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+                                    s_w);
+  else
+    contract_dispatch<kTxt, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+                                    s_w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// expand + decode
+// ---------------------------------------------------------------------------
+constexpr int kEWaves = 4;
+constexpr int kEThreads = kEWaves * kWave;
+
+struct ExpandParams {
+  const uint8_t* mv;
+  const uint8_t* mt;
+  int B, H, W, R, S, Ho, Wo;
+  int wpg;               // rows (waves) per workgroup
+  int groups_per_crop;   // ceil(R / wpg)
+  uint64_t magic_w;      // ceil(2^32 / W): c / W == (c * magic_w) >> 32 for c * W < 2^32
+  float* heat;
+  int32_t* idx;
+  float* xy;
+  float* score;
+};
+
+// The 16 outputs of low-res cell (i, j): rows 4i .. 4i+3, columns 4j ..
+// 4j+3, raster order. Half-pixel 4x bilinear weights: each output lies
+// 3/8 or 1/8 of a cell from its own cell centre toward a neighbour, so it
+// is centre + w * (neighbour - centre); at a clamped border the neighbour is
+// the cell itself and the output is the centre exactly.
+__device__ __forceinline__ void cell_values(const float* P, int i, int j, int H, int W,
+                                            float (&o)[16]) {
+  const int im = i > 0 ? i - 1 : 0, ip = i < H - 1 ? i + 1 : i;
+  const int jm = j > 0 ? j - 1 : 0, jp = j < W - 1 ? j + 1 : j;
+  float h[3][4];
+  const int rows[3] = {im, i, ip};
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const float* pr = P + rows[r] * W;
+    const float a = pr[jm], c = pr[j], e = pr[jp];
+    const float dl = a - c, dr = e - c;
+    h[r][0] = fmaf(dl, 0.375f, c);
+    h[r][1] = fmaf(dl, 0.125f, c);
+    h[r][2] = fmaf(dr, 0.125f, c);
+    h[r][3] = fmaf(dr, 0.375f, c);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float c = h[1][e], du = h[0][e] - c, dd = h[2][e] - c;
+    o[0 + e] = fmaf(du, 0.375f, c);
+    o[4 + e] = fmaf(du, 0.125f, c);
+    o[8 + e] = fmaf(dd, 0.125f, c);
+    o[12 + e] = fmaf(dd, 0.375f, c);
+  }
+}
+
+__device__ __forceinline__ float max16(const float (&o)[16]) {
+  float m01 = fmaxf(fmaxf(o[0], o[1]), fmaxf(o[2], o[3]));
+  float m23 = fmaxf(fmaxf(o[4], o[5]), fmaxf(o[6], o[7]));
+  float m45 = fmaxf(fmaxf(o[8], o[9]), fmaxf(o[10], o[11]));
+  float m67 = fmaxf(fmaxf(o[12], o[13]), fmaxf(o[14], o[15]));
+  return fmaxf(fmaxf(m01, m23), fmaxf(m45, m67));
+}
+
+// first raster position of value m among o[0..15]
+__device__ __forceinline__ int first_of(const float (&o)[16], float m) {
+  int sel = 15;
+#pragma unroll
+  for (int q = 14; q >= 0; --q) sel = (o[q] == m) ? q : sel;
+  return sel;
+}
+
+// SMALLW (W <= 64): a lane's cells c, c + 64, ... lie on increasing cell
+// rows, so every output of a later cell has a larger flat index than any
+// output of an earlier one; the lane keeps (best value, its cell) with a
+// strict > and finds the position inside the cell once, at the end.
+template <bool SMALLW>
+__global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
+  extern __shared__ __align__(16) float lds_p[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const ItemCoord ic = xcd_item(blockIdx.x, p.groups_per_crop);
+  const int b = ic.crop;
+  if (b >= p.B || wave >= p.wpg) return;
+  const uint8_t* mv = p.mv ? p.mv + (size_t)b * p.R : nullptr;
+  const uint8_t* mt = p.mt ? p.mt + (size_t)b * p.R : nullptr;
+
+  if (ic.item == 0 && wave == 0 && p.idx) {
+    for (int r = lane; r < p.R; r += kWave) {
+      if (!((mv && mv[r]) || (mt && mt[r]))) {
+        const size_t o = (size_t)b * p.R + r;
+        p.idx[o] = -1;
+        p.xy[2 * o] = __builtin_nanf("");
+        p.xy[2 * o + 1] = __builtin_nanf("");
+        p.score[o] = -INFINITY;
+      }
+    }
+  }
+
+  // this wave's row: the rank-th valid row of the crop
+  int rank = ic.item * p.wpg + wave;
+  int row = -1;
+  for (int base = 0; base < p.R; base += kWave) {
+    const int r = base + lane;
+    const bool v = r < p.R && ((mv && mv[r]) || (mt && mt[r]));
+    const uint64_t bal = __ballot(v);
+    const int cnt = __popcll(bal);
+    if (rank < cnt) {
+      const int below = __popcll(bal & ((1ull << lane) - 1ull));
+      const uint64_t hit = __ballot(v && below == rank);
+      row = base + __builtin_ctzll(hit);
+      break;
+    }
+    rank -= cnt;
+  }
+  if (row < 0) return;
+
+  const size_t hw_out = (size_t)p.Ho * p.Wo;
+  float* out = p.heat + ((size_t)b * p.R + row) * hw_out;
+  float* P = lds_p + (size_t)wave * p.S;
+  // the parked low-res map -> LDS (this wave only); every load has returned
+  // before the first store below can overwrite it
+  for (int v = lane; 4 * v < p.S; v += kWave)
+    reinterpret_cast<f32x4*>(P)[v] = reinterpret_cast<const f32x4*>(out)[v];
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+
+  float bv = -INFINITY;
+  int bi = INT_MAX;  // SMALLW: best cell; otherwise best flat index
+  for (int c = lane; c < p.S; c += kWave) {
+    const int i = (int)(((uint64_t)(uint32_t)c * p.magic_w) >> 32), j = c - i * p.W;
+    float o[16];
+    cell_values(P, i, j, p.H, p.W, o);
+    float* dst = out + (size_t)(4 * i) * p.Wo + 4 * j;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      __builtin_nontemporal_store(f32x4{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]},
+                                  reinterpret_cast<f32x4*>(dst + (size_t)d * p.Wo));
+    const float m = max16(o);
+    if (SMALLW) {
+      if (m > bv) {
+        bv = m;
+        bi = c;
+      }
+    } else {
+      const int q = first_of(o, m);
+      const int flat = (4 * i + (q >> 2)) * p.Wo + 4 * j + (q & 3);
+      if (better(m, flat, bv, bi)) {
+        bv = m;
+        bi = flat;
+      }
+    }
+  }
+  if (!p.idx) return;
+  if (SMALLW) {
+    if (bi != INT_MAX) {
+      const int c = bi;
+      const int i = (int)(((uint64_t)(uint32_t)c * p.magic_w) >> 32), j = c - i * p.W;
+      float o[16];
+      cell_values(P, i, j, p.H, p.W, o);
+      const int q = first_of(o, bv);
+      bi = (4 * i + (q >> 2)) * p.Wo + 4 * j + (q & 3);
+    }
+  }
+  wave_argmax(bv, bi);
+  if (lane == 0) {
+    const size_t o = (size_t)b * p.R + row;
+    const int y = bi / p.Wo, x = bi - y * p.Wo;
+    p.idx[o] = bi;
+    p.xy[2 * o] = (float)(2 * x + 1) / (float)p.Wo - 1.f;
+    p.xy[2 * o + 1] = (float)(2 * y + 1) / (float)p.Ho - 1.f;
+    p.score[o] = bv;
+  }
+}
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+bool heatmap_stream_applicable(int C, int S, bool bf16) {
+  return bf16 && C % kKS == 0 && S % 16 == 0 && S <= kHeatmapMaxS;
+}
+
+StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
+  StreamPlan sp;
+  // wave groups per chunk: the fewest that still cover a small map in one
+  // chunk, then fewer still while the batch leaves CUs idle
+  static const int kNgSteps[] = {12, 6, 4, 3, 2, 1};
+  int k = 0;
+  while (k + 1 < 6 && kNgSteps[k + 1] * kGroupPx >= S) ++k;
+  const int rblocks = ceil_div(R, kItemRows);
+  while (k + 1 < 6 &&
+         (long long)B * ceil_div(S, kNgSteps[k] * kGroupPx) * rblocks < 240)
+    ++k;
+  sp.ng = kNgSteps[k];
+  sp.chunk_px = sp.ng * kGroupPx;
+  sp.nchunks = ceil_div(S, sp.chunk_px);
+  sp.rblocks = rblocks;
+  // a dual-prompt block with more than 3 M tiles needs ceil(MH * ng / 12)
+  // <= 3 wave units: true for ng <= 6; with ng = 12 it takes half chunks
+  sp.halves = sp.ng == 12 ? 2 : 1;
+  // LDS of an item: three feature slots and five kernel-row slots
+  int max_instr = 0;
+  size_t max_lds = 0;
+  auto need = [&](int chunk_px, int arows) {
+    const int nfi = ceil_div(kKS * (chunk_px / 8 + 1), kWave);
+    const int nai = ceil_div(arows * kRowSlots, kWave);
+    if (nfi + nai > max_instr) max_instr = nfi + nai;
+    const size_t lds = (size_t)(kFStages * nfi + kAStages * nai) * 1024;
+    if (lds > max_lds) max_lds = lds;
+  };
+  need(sp.chunk_px, sp.halves == 2 ? 2 * 16 * kMaxDualUnits : 2 * kItemRows);
+  need(sp.chunk_px, kItemRows);
+  if (sp.halves == 2) need(sp.chunk_px / 2, 2 * kItemRows);
+  sp.contract_lds = max_lds;
+  sp.wpg = S <= 4096 ? kEWaves : 1;
+  sp.expand_lds = (size_t)sp.wpg * S * sizeof(float);
+  sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kLdsBudget &&
+          sp.expand_lds <= 64 * 1024;
+  return sp;
+}
+
+hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
+  const int S = a.H * a.W;
+  const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R);
+  if (!sp.ok) return hipErrorInvalidConfiguration;
+  const long long crops_pad = (long long)(a.B + kXcds - 1) / kXcds * kXcds;
+
+  ContractParams cp;
+  cp.query = static_cast<const uint16_t*>(a.query);
+  cp.kv = static_cast<const uint16_t*>(a.kv);
+  cp.mv = a.mv;
+  cp.kt = static_cast<const uint16_t*>(a.kt);
+  cp.mt = a.mt;
+  cp.B = a.B;
+  cp.C = a.C;
+  cp.H = a.H;
+  cp.W = a.W;
+  cp.R = a.R;
+  cp.S = S;
+  cp.ng = sp.ng;
+  cp.chunk_px = sp.chunk_px;
+  cp.nchunks = sp.nchunks;
+  cp.rblocks = sp.rblocks;
+  cp.items_per_crop = sp.nchunks * sp.rblocks;
+  cp.nsteps = a.C / kKS;
+  cp.halves = sp.halves;
+  cp.lds_bytes = (int)sp.contract_lds;
+  cp.heat = a.heat;
+  const long long cgrid = crops_pad * cp.items_per_crop;
+  if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(contract_kernel, dim3((unsigned)cgrid), dim3(kCThreads), sp.contract_lds,
+                     stream, cp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  ExpandParams ep;
+  ep.mv = a.mv;
+  ep.mt = a.mt;
+  ep.B = a.B;
+  ep.H = a.H;
+  ep.W = a.W;
+  ep.R = a.R;
+  ep.S = S;
+  ep.Ho = 4 * a.H;
+  ep.Wo = 4 * a.W;
+  ep.wpg = sp.wpg;
+  ep.groups_per_crop = ceil_div(a.R, sp.wpg);
+  ep.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
+  ep.heat = a.heat;
+  ep.idx = a.idx;
+  ep.xy = a.xy;
+  ep.score = a.score;
+  const long long egrid = crops_pad * ep.groups_per_crop;
+  if (egrid > INT_MAX) return hipErrorInvalidConfiguration;
+  if (a.W <= kWave)
+    hipLaunchKernelGGL((expand_kernel<true>), dim3((unsigned)egrid), dim3(kEThreads),
+                       sp.expand_lds, stream, ep);
+  else
+    hipLaunchKernelGGL((expand_kernel<false>), dim3((unsigned)egrid), dim3(kEThreads),
+                       sp.expand_lds, stream, ep);
+  return hipGetLastError();
+}
+
+}  // namespace gkd

@@ -43,7 +43,7 @@ struct DecodeArgs {
 // Shape limits of the heatmap kernel: its LDS holds the fused low-res maps
 // of at least one row (S floats).
 constexpr int kHeatmapMaxS = 16384;
-constexpr size_t kLdsBudget = 150 * 1024;  // of 160 KiB; the rest is static
+constexpr size_t kLdsBudget = 156 * 1024;  // of 160 KiB; the rest is static
 
 struct HeatmapPlan {
   int nsteps = 0;         // K steps over the channels
@@ -53,9 +53,17 @@ struct HeatmapPlan {
 HeatmapPlan plan_heatmap(int C, int S, bool bf16);
 
 hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream);
-// bf16 fast path (direct-to-LDS staging, transposing LDS reads)
-bool heatmap_lds_applicable(int C, int S, bool bf16);
-hipError_t launch_heatmap_lds(const HeatmapArgs& a, hipStream_t stream);
+// bf16 path in two launches: contraction (all rows of a crop per
+// workgroup, low-res maps parked in the heatmap rows), then expand + decode
+// (one wave per valid row)
+struct StreamPlan {
+  int ng = 0, chunk_px = 0, nchunks = 0, rblocks = 0, halves = 1, wpg = 0;
+  size_t contract_lds = 0, expand_lds = 0;
+  bool ok = false;
+};
+bool heatmap_stream_applicable(int C, int S, bool bf16);
+StreamPlan plan_heatmap_stream(int B, int C, int S, int R);
+hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream);
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

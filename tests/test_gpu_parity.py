@@ -227,13 +227,15 @@ def test_chain_vkp_heatmap_decode(gkd, ora):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(3, 40, 5, 7, 19), (2, 3, 1, 1, 4), (2, 72, 9, 10, 33),
                                    (5, 256, 24, 24, 80), (1, 1, 2, 3, 2), (3, 64, 8, 8, 16),
-                                   (2, 96, 16, 16, 40), (9, 128, 24, 24, 37)])
+                                   (2, 96, 16, 16, 40), (9, 128, 24, 24, 37),
+                                   (2, 64, 32, 32, 8), (1, 32, 2, 72, 6), (2, 64, 8, 8, 200)])
 def test_ragged_shapes(gkd, ora, dtype, shape):
-    """Ragged channel counts, maps that do not fill a 64-pixel super-tile,
+    """Ragged channel counts, maps that do not fill a pixel chunk,
     degenerate 1x1 maps, random masks (dual, single, none). The bf16 shapes
-    with C % 32 == 0 and H*W a multiple of 64 up to 576 take the LDS-staged
-    kernel (one and two M tiles per modality, idle waves); the rest take
-    the general kernel."""
+    with C % 32 == 0 and H*W % 16 == 0 take the two-launch path
+    (contraction + expand): several pixel chunks (32x32), rows wider than a
+    wave (W = 72), more valid rows than one item holds (R = 200, up to four
+    row blocks), idle waves; the rest take the general kernel."""
     B, C, H, W, R = shape
     rng = np.random.default_rng(B * 1000 + C + H * 10 + W + R)
     q = rng.standard_normal((B, C, H, W)).astype(np.float32)
