@@ -37,13 +37,129 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 // ---------------------------------------------------------------------------
+// row expansion
+// ---------------------------------------------------------------------------
+// The 16 outputs of low-res cell (i, j): rows 4i .. 4i+3, columns 4j ..
+// 4j+3, raster order. Half-pixel 4x bilinear weights: each output lies
+// 3/8 or 1/8 of a cell from its own cell centre toward a neighbour, so it
+// is centre + w * (neighbour - centre); at a clamped border the neighbour is
+// the cell itself and the output is the centre exactly.
+__device__ __forceinline__ void cell_values(const float* P, int i, int j, int H, int W,
+                                            float (&o)[16]) {
+  const int im = i > 0 ? i - 1 : 0, ip = i < H - 1 ? i + 1 : i;
+  const int jm = j > 0 ? j - 1 : 0, jp = j < W - 1 ? j + 1 : j;
+  float h[3][4];
+  const int rows[3] = {im, i, ip};
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const float* pr = P + rows[r] * W;
+    const float a = pr[jm], c = pr[j], e = pr[jp];
+    const float dl = a - c, dr = e - c;
+    h[r][0] = fmaf(dl, 0.375f, c);
+    h[r][1] = fmaf(dl, 0.125f, c);
+    h[r][2] = fmaf(dr, 0.125f, c);
+    h[r][3] = fmaf(dr, 0.375f, c);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float c = h[1][e], du = h[0][e] - c, dd = h[2][e] - c;
+    o[0 + e] = fmaf(du, 0.375f, c);
+    o[4 + e] = fmaf(du, 0.125f, c);
+    o[8 + e] = fmaf(dd, 0.125f, c);
+    o[12 + e] = fmaf(dd, 0.375f, c);
+  }
+}
+
+__device__ __forceinline__ float max16(const float (&o)[16]) {
+  float m01 = fmaxf(fmaxf(o[0], o[1]), fmaxf(o[2], o[3]));
+  float m23 = fmaxf(fmaxf(o[4], o[5]), fmaxf(o[6], o[7]));
+  float m45 = fmaxf(fmaxf(o[8], o[9]), fmaxf(o[10], o[11]));
+  float m67 = fmaxf(fmaxf(o[12], o[13]), fmaxf(o[14], o[15]));
+  return fmaxf(fmaxf(m01, m23), fmaxf(m45, m67));
+}
+
+// first raster position of value m among o[0..15]
+__device__ __forceinline__ int first_of(const float (&o)[16], float m) {
+  int sel = 15;
+#pragma unroll
+  for (int q = 14; q >= 0; --q) sel = (o[q] == m) ? q : sel;
+  return sel;
+}
+
+struct RowGeom {
+  int H, W, S, Ho, Wo;
+  uint64_t magic_w;  // ceil(2^32 / W): c / W == (c * magic_w) >> 32 for c * W < 2^32
+};
+
+// One wave expands the low-res map P (row-major H x W, in LDS) of one row
+// into out ([4H][4W]) with 16-byte non-temporal stores and leaves the
+// row's first-occurrence argmax (value, flat index) in every lane.
+// SMALLW (W <= 64): a lane's cells c, c + 64, ... lie on increasing cell
+// rows, so every output of a later cell has a larger flat index than any
+// output of an earlier one; the lane keeps (best value, its cell) with a
+// strict > and finds the position inside the cell once, at the end.
+template <bool SMALLW>
+__device__ __forceinline__ void expand_row(const float* P, float* out, const RowGeom& g, int lane,
+                                           bool decode, float& best_v, int& best_i) {
+  float bv = -INFINITY;
+  int bi = INT_MAX;  // SMALLW: best cell; otherwise best flat index
+  for (int c = lane; c < g.S; c += kWave) {
+    const int i = (int)(((uint64_t)(uint32_t)c * g.magic_w) >> 32), j = c - i * g.W;
+    float o[16];
+    cell_values(P, i, j, g.H, g.W, o);
+    float* dst = out + (size_t)(4 * i) * g.Wo + 4 * j;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      __builtin_nontemporal_store(f32x4{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]},
+                                  reinterpret_cast<f32x4*>(dst + (size_t)d * g.Wo));
+    const float m = max16(o);
+    if (SMALLW) {
+      if (m > bv) {
+        bv = m;
+        bi = c;
+      }
+    } else {
+      const int q = first_of(o, m);
+      const int flat = (4 * i + (q >> 2)) * g.Wo + 4 * j + (q & 3);
+      if (better(m, flat, bv, bi)) {
+        bv = m;
+        bi = flat;
+      }
+    }
+  }
+  if (!decode) return;
+  if (SMALLW && bi != INT_MAX) {
+    const int c = bi;
+    const int i = (int)(((uint64_t)(uint32_t)c * g.magic_w) >> 32), j = c - i * g.W;
+    float o[16];
+    cell_values(P, i, j, g.H, g.W, o);
+    const int q = first_of(o, bv);
+    bi = (4 * i + (q >> 2)) * g.Wo + 4 * j + (q & 3);
+  }
+  wave_argmax(bv, bi);
+  best_v = bv;
+  best_i = bi;
+}
+
+// keypoint record of one row: flat index, cell-centre -1..1 coordinates,
+// raw score
+__device__ __forceinline__ void write_keypoint(int32_t* idx, float* xy, float* score, size_t o,
+                                               float bv, int bi, int Ho, int Wo) {
+  const int y = bi / Wo, x = bi - y * Wo;
+  idx[o] = bi;
+  xy[2 * o] = (float)(2 * x + 1) / (float)Wo - 1.f;
+  xy[2 * o + 1] = (float)(2 * y + 1) / (float)Ho - 1.f;
+  score[o] = bv;
+}
+
+// ---------------------------------------------------------------------------
 // contraction
 // ---------------------------------------------------------------------------
 constexpr int kCWaves = 12;
 constexpr int kCThreads = kCWaves * kWave;  // 768
 constexpr int kKS = 32;                     // channels per K step (one MFMA K)
-constexpr int kFStages = 3;                 // feature ring: loads run 2 steps ahead
-constexpr int kAStages = 5;                 // kernel-row ring: loads run 4 steps ahead
+constexpr int kMinStages = 3;               // LDS ring slots per item (loads run
+constexpr int kMaxStages = 6;               // stages - 1 steps ahead), as LDS allows
 constexpr int kGroupPx = 48;                // one wave unit: 3 N tiles of 16 pixels
 constexpr int kItemRows = 80;               // valid rows per item
 constexpr int kMaxMH = kItemRows / 16;      // M tiles per modality
@@ -87,6 +203,16 @@ __device__ __forceinline__ void wait_vmcnt_upto(int n) {
     case 8: wait_vmcnt<8>(); break;
     case 9: wait_vmcnt<9>(); break;
     case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
+    case 17: wait_vmcnt<17>(); break;
+    case 18: wait_vmcnt<18>(); break;
+    case 19: wait_vmcnt<19>(); break;
+    case 20: wait_vmcnt<20>(); break;
     default: wait_vmcnt<0>(); break;
   }
 }
@@ -169,6 +295,7 @@ struct ItemShape {
   int arows;   // kernel rows staged per step: nmod * MH * 16
   int fbytes;  // feature slot (whole 1 KiB blocks)
   int abytes;  // kernel-row slot (whole 1 KiB blocks)
+  int stages;  // LDS ring slots
   int px0;     // first pixel of the chunk
   bool has_v;
 };
@@ -214,24 +341,25 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   const int nrow = tid >> 2, ncol = tid & 3;
   float ss = 0.f;
 
-  unsigned char* const aring = lds + (size_t)kFStages * it.fbytes;
+  unsigned char* const aring = lds + (size_t)it.stages * it.fbytes;
+  const int ahead = it.stages - 1;  // loads run this many steps ahead
   for (int k = 0; k < p.nsteps; ++k) {
     if (k > 0) {
-      // features of step k and kernel rows of step k (issued earlier) have
-      // landed for this wave once at most these younger loads remain:
-      // rows k+2, features k+1, rows k+3 (those that were issued)
-      const int younger = (k + 1 < p.nsteps ? pl.nf : 0) + (k + 2 < p.nsteps ? pl.na : 0) +
-                          (k + 3 < p.nsteps ? pl.na : 0);
-      wait_vmcnt_upto(younger);
+      // step k (features, then kernel rows) has landed for this wave once at
+      // most the loads of the younger steps issued so far remain
+      const int younger = min(ahead - 1, p.nsteps - 1 - k);
+      wait_vmcnt_upto(younger * (pl.nf + pl.na));
     }
     lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
-    if (k + 2 < p.nsteps)
-      issue_features(pl, bs, lds + (size_t)((k + 2) % kFStages) * it.fbytes, wave, k + 2);
-    if (k + 4 < p.nsteps)
-      issue_rows(pl, bs, aring + (size_t)((k + 4) % kAStages) * it.abytes, k + 4);
+    if (k + ahead < p.nsteps) {
+      const int slot = (k + ahead) % it.stages;
+      issue_features(pl, bs, lds + (size_t)slot * it.fbytes, wave, k + ahead);
+      issue_rows(pl, bs, aring + (size_t)slot * it.abytes, k + ahead);
+    }
 
-    const unsigned char* sb = lds + (size_t)(k % kFStages) * it.fbytes;
-    const unsigned char* sa = aring + (size_t)(k % kAStages) * it.abytes;
+    const int cur = k % it.stages;
+    const unsigned char* sb = lds + (size_t)cur * it.fbytes;
+    const unsigned char* sa = aring + (size_t)cur * it.abytes;
     // B: lane (n16, g4) of N tile t receives channels 8 g4 .. 8 g4 + 7 of
     // pixel gpx + 16 t + n16 from two transposing 8-byte reads (rows
     // 8 g4 + n16/4 and +4, columns 4 (n16 % 4) .. +3 of the tile)
@@ -332,11 +460,9 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     for (int e = tid; e < nrows * q4; e += kCThreads) {
       const int r = e / q4, c4 = e - r * q4;
       const int px = it.px0 + 4 * c4;
-      if (px < p.S) {
-        const f32x4 val = *reinterpret_cast<const f32x4*>(Pl + r * pitch + 4 * c4);
+      if (px < p.S)
         *reinterpret_cast<f32x4*>(p.heat + ((size_t)b * p.R + s_rows[base + r]) * hw_out + px) =
-            val;
-      }
+            *reinterpret_cast<const f32x4*>(Pl + r * pitch + 4 * c4);
     }
     lds_barrier();
   }
@@ -460,11 +586,14 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
     pl.off[i] = off;
     pl.kinds |= kind << (2 * i);
   }
-  unsigned char* const aring = lds + (size_t)kFStages * it.fbytes;
-  issue_features(pl, bs, lds, wave, 0);
-  if (p.nsteps > 1) issue_features(pl, bs, lds + it.fbytes, wave, 1);
-  for (int st = 0; st < kAStages - 1 && st < p.nsteps; ++st)
+  // as many ring slots as the workgroup's LDS holds, within [3, 6]
+  it.stages = p.lds_bytes / (it.fbytes + it.abytes);
+  it.stages = it.stages < kMinStages ? kMinStages : (it.stages > kMaxStages ? kMaxStages : it.stages);
+  unsigned char* const aring = lds + (size_t)it.stages * it.fbytes;
+  for (int st = 0; st < it.stages - 1 && st < p.nsteps; ++st) {
+    issue_features(pl, bs, lds + (size_t)st * it.fbytes, wave, st);
     issue_rows(pl, bs, aring + (size_t)st * it.abytes, st);
+  }
   wait_vmcnt<0>();  // the prologue steps
 
   const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
@@ -492,64 +621,14 @@ struct ExpandParams {
   int B, H, W, R, S, Ho, Wo;
   int wpg;               // rows (waves) per workgroup
   int groups_per_crop;   // ceil(R / wpg)
-  uint64_t magic_w;      // ceil(2^32 / W): c / W == (c * magic_w) >> 32 for c * W < 2^32
+  uint64_t magic_w;      // ceil(2^32 / W)
   float* heat;
   int32_t* idx;
   float* xy;
   float* score;
 };
 
-// The 16 outputs of low-res cell (i, j): rows 4i .. 4i+3, columns 4j ..
-// 4j+3, raster order. Half-pixel 4x bilinear weights: each output lies
-// 3/8 or 1/8 of a cell from its own cell centre toward a neighbour, so it
-// is centre + w * (neighbour - centre); at a clamped border the neighbour is
-// the cell itself and the output is the centre exactly.
-__device__ __forceinline__ void cell_values(const float* P, int i, int j, int H, int W,
-                                            float (&o)[16]) {
-  const int im = i > 0 ? i - 1 : 0, ip = i < H - 1 ? i + 1 : i;
-  const int jm = j > 0 ? j - 1 : 0, jp = j < W - 1 ? j + 1 : j;
-  float h[3][4];
-  const int rows[3] = {im, i, ip};
-#pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    const float* pr = P + rows[r] * W;
-    const float a = pr[jm], c = pr[j], e = pr[jp];
-    const float dl = a - c, dr = e - c;
-    h[r][0] = fmaf(dl, 0.375f, c);
-    h[r][1] = fmaf(dl, 0.125f, c);
-    h[r][2] = fmaf(dr, 0.125f, c);
-    h[r][3] = fmaf(dr, 0.375f, c);
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float c = h[1][e], du = h[0][e] - c, dd = h[2][e] - c;
-    o[0 + e] = fmaf(du, 0.375f, c);
-    o[4 + e] = fmaf(du, 0.125f, c);
-    o[8 + e] = fmaf(dd, 0.125f, c);
-    o[12 + e] = fmaf(dd, 0.375f, c);
-  }
-}
-
-__device__ __forceinline__ float max16(const float (&o)[16]) {
-  float m01 = fmaxf(fmaxf(o[0], o[1]), fmaxf(o[2], o[3]));
-  float m23 = fmaxf(fmaxf(o[4], o[5]), fmaxf(o[6], o[7]));
-  float m45 = fmaxf(fmaxf(o[8], o[9]), fmaxf(o[10], o[11]));
-  float m67 = fmaxf(fmaxf(o[12], o[13]), fmaxf(o[14], o[15]));
-  return fmaxf(fmaxf(m01, m23), fmaxf(m45, m67));
-}
-
-// first raster position of value m among o[0..15]
-__device__ __forceinline__ int first_of(const float (&o)[16], float m) {
-  int sel = 15;
-#pragma unroll
-  for (int q = 14; q >= 0; --q) sel = (o[q] == m) ? q : sel;
-  return sel;
-}
-
-// SMALLW (W <= 64): a lane's cells c, c + 64, ... lie on increasing cell
-// rows, so every output of a later cell has a larger flat index than any
-// output of an earlier one; the lane keeps (best value, its cell) with a
-// strict > and finds the position inside the cell once, at the end.
+// One wave per valid row of the crop (by rank).
 template <bool SMALLW>
 __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   extern __shared__ __align__(16) float lds_p[];
@@ -600,52 +679,11 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
     reinterpret_cast<f32x4*>(P)[v] = reinterpret_cast<const f32x4*>(out)[v];
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
-  float bv = -INFINITY;
-  int bi = INT_MAX;  // SMALLW: best cell; otherwise best flat index
-  for (int c = lane; c < p.S; c += kWave) {
-    const int i = (int)(((uint64_t)(uint32_t)c * p.magic_w) >> 32), j = c - i * p.W;
-    float o[16];
-    cell_values(P, i, j, p.H, p.W, o);
-    float* dst = out + (size_t)(4 * i) * p.Wo + 4 * j;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      __builtin_nontemporal_store(f32x4{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]},
-                                  reinterpret_cast<f32x4*>(dst + (size_t)d * p.Wo));
-    const float m = max16(o);
-    if (SMALLW) {
-      if (m > bv) {
-        bv = m;
-        bi = c;
-      }
-    } else {
-      const int q = first_of(o, m);
-      const int flat = (4 * i + (q >> 2)) * p.Wo + 4 * j + (q & 3);
-      if (better(m, flat, bv, bi)) {
-        bv = m;
-        bi = flat;
-      }
-    }
-  }
-  if (!p.idx) return;
-  if (SMALLW) {
-    if (bi != INT_MAX) {
-      const int c = bi;
-      const int i = (int)(((uint64_t)(uint32_t)c * p.magic_w) >> 32), j = c - i * p.W;
-      float o[16];
-      cell_values(P, i, j, p.H, p.W, o);
-      const int q = first_of(o, bv);
-      bi = (4 * i + (q >> 2)) * p.Wo + 4 * j + (q & 3);
-    }
-  }
-  wave_argmax(bv, bi);
-  if (lane == 0) {
-    const size_t o = (size_t)b * p.R + row;
-    const int y = bi / p.Wo, x = bi - y * p.Wo;
-    p.idx[o] = bi;
-    p.xy[2 * o] = (float)(2 * x + 1) / (float)p.Wo - 1.f;
-    p.xy[2 * o + 1] = (float)(2 * y + 1) / (float)p.Ho - 1.f;
-    p.score[o] = bv;
-  }
+  const RowGeom g{p.H, p.W, p.S, p.Ho, p.Wo, p.magic_w};
+  float bv;
+  int bi;
+  expand_row<SMALLW>(P, out, g, lane, p.idx != nullptr, bv, bi);
+  if (p.idx && lane == 0) write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + row, bv, bi, p.Ho, p.Wo);
 }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -681,13 +719,15 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
     const int nfi = ceil_div(kKS * (chunk_px / 8 + 1), kWave);
     const int nai = ceil_div(arows * kRowSlots, kWave);
     if (nfi + nai > max_instr) max_instr = nfi + nai;
-    const size_t lds = (size_t)(kFStages * nfi + kAStages * nai) * 1024;
+    const size_t lds = (size_t)(kMinStages * nfi + kMinStages * nai) * 1024;
     if (lds > max_lds) max_lds = lds;
   };
   need(sp.chunk_px, sp.halves == 2 ? 2 * 16 * kMaxDualUnits : 2 * kItemRows);
   need(sp.chunk_px, kItemRows);
   if (sp.halves == 2) need(sp.chunk_px / 2, 2 * kItemRows);
-  sp.contract_lds = max_lds;
+  // one workgroup per CU whatever its LDS (registers decide that), so an
+  // item may deepen its ring into the whole budget
+  sp.contract_lds = max_lds <= kLdsBudget ? kLdsBudget : max_lds;
   sp.wpg = S <= 4096 ? kEWaves : 1;
   sp.expand_lds = (size_t)sp.wpg * S * sizeof(float);
   sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kLdsBudget &&

@@ -104,7 +104,7 @@ def sample_crops(d, n):
 
 
 CASES = [("tiny_visual", {}, None), ("text_f32", {}, None), ("dual_bf16", {}, 6),
-         ("longtail_bf16", {}, 8), ("highres_bf16", {}, 2)]
+         ("longtail_bf16", {}, 8), ("highres_bf16", {}, 2), ("longtail_dense", {}, 3)]
 
 
 @pytest.mark.parametrize("name,kw,nsample", CASES, ids=[c[0] for c in CASES])
@@ -155,6 +155,24 @@ def test_kernel_heatmap_parity(gkd, ora, name, kw, nsample):
     gi = heat.view(torch.int32).cpu().numpy()
     assert np.all(gi[valid == 0] == NAN_BITS)
     assert np.all(idx.cpu().numpy()[valid == 0] == -1)
+
+
+@pytest.mark.parametrize("name", ["longtail_bf16", "longtail_dense"])
+def test_every_valid_row_finished(gkd, name):
+    """Full batch, every row: whether the contraction kernel expanded a row
+    itself or parked it for the expand kernel, the row ends finite
+    everywhere (no parked map or tag is left behind) and its keypoint is
+    set; rows with no prompt keep their bytes."""
+    d = workload(name)
+    protos = gkdsynth.round_bf16_f32(np.asarray(
+        np.random.default_rng(6).standard_normal((d["B"], d["R"], d["C"])), np.float32))
+    print(f"[finished] {name}", flush=True)
+    heat, (idx, xy, score) = run_heatmap(gkd, d, protos)
+    v = dev_tensor(valid_rows(d)).bool()
+    rows = heat.view(d["B"], d["R"], -1)
+    assert bool(torch.isfinite(rows[v]).all())
+    assert bool((idx[v] >= 0).all()) and bool(torch.isfinite(score[v]).all())
+    assert bool((rows.view(torch.int32)[~v] == NAN_BITS).all())
 
 
 def test_fused_decode_equals_standalone_decode(gkd):
