@@ -214,9 +214,17 @@ __global__ __launch_bounds__(kVThreads) void vkp_kernel(VkParams p) {
 // The inner sum is one MFMA per image row with K = j (W <= 32 columns, one
 // 16-byte load of 8 pixels per lane, straight from HBM), A = wx as hi + lo
 // bfloat16 parts (constant over the whole item, held in registers); the
-// outer sum is an fp32 fma per row. One workgroup = (crop, 256 channels,
-// all of the crop's valid rows up to 80): every support byte is read once.
-// Wave w owns channel tile w (16 channels) for every M tile.
+// outer sum is an fp32 fma per row. Item = (crop, block of up to 80 valid
+// rows, 128 channels); wave w owns channel tile w (16 channels) for every
+// M tile, so every support byte is read once.
+//
+// Persistent and pipelined: the grid is two workgroups per CU. Each
+// workgroup first lists the (crop, row block) pairs that hold valid rows
+// (crops without a visual prompt cost nothing after that), then walks the
+// items k = blockIdx.x, + gridDim.x, ... While item k streams, the masks
+// and keypoints of the next item are in flight, and the last ring refills
+// of item k already fetch the first image rows of the next one, so the
+// row selection and weight set-up between items overlap the HBM stream.
 // ---------------------------------------------------------------------------
 constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;  // 512
@@ -224,16 +232,20 @@ constexpr int kFRows = 80;                  // valid rows per item
 constexpr int kFMaxMT = kFRows / 16;
 constexpr int kFMaxHW = 32;                 // H, W <= 32
 constexpr int kFCh = kFWaves * 16;          // channels per item
-constexpr int kFDepth = 6;                  // image rows loaded ahead per wave
+constexpr int kFDepth = 4;                  // image rows loaded ahead per wave
 constexpr int kFMaxR = 256;                 // R <= 256 (masks and keypoints staged in LDS)
+constexpr int kFList = 4096;                // (crop, row block) pairs per launch
+constexpr int kFWgPerCu = 2;                // resident workgroups per CU (4 waves per SIMD)
 
 struct VkFastParams {
   const uint16_t* support;
   const float* kpts;
   const uint8_t* valid;
   int B, C, H, W, R, S;
+  bool chain;  // H % kFDepth == 0: the ring runs on into the next item
   float stride, inv2s2;
-  int cblocks, items_per_crop;
+  int cblocks;
+  bool mask_words;  // R % 4 == 0 and the mask base 4-byte aligned
   uint16_t* protos;
 };
 
@@ -246,13 +258,57 @@ __device__ __forceinline__ void lds_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Number of set mask bytes of one crop.
+__device__ __forceinline__ int count_valid(const VkFastParams& p, int b) {
+  int cnt = 0;
+  if (p.mask_words) {
+    const uint32_t* v = reinterpret_cast<const uint32_t*>(p.valid + (size_t)b * p.R);
+#pragma unroll 4
+    for (int q = 0; q < p.R / 4; ++q) {
+      const uint32_t w = v[q];
+      // high bit of each byte set iff that byte is nonzero
+      const uint32_t t = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
+      cnt += __popc(t);
+    }
+  } else {
+    const uint8_t* v = p.valid + (size_t)b * p.R;
+#pragma unroll 8
+    for (int r = 0; r < p.R; ++r) cnt += v[r] != 0;
+  }
+  return cnt;
+}
+
+// One item's image rows: the wave's 16 channels start at a wave-uniform
+// base; lane (n16, g4) adds a fixed byte offset for channel n16 and columns
+// 8 g4 .. 8 g4 + 7 (lanes past the row's columns re-read column 0 and
+// contribute zeros).
+__device__ __forceinline__ const char* item_base(const VkFastParams& p, int b, int c0) {
+  return reinterpret_cast<const char*>(p.support + ((size_t)b * p.C + c0) * p.S);
+}
+__device__ __forceinline__ u32x4 load_row(const char* base, uint32_t loff) {
+  return *reinterpret_cast<const u32x4*>(base + loff);
+}
+
+// Streams one item through the ring and writes its prototypes. The ring
+// enters holding rows 0 .. kFDepth-1 of this item (slot = row mod kFDepth)
+// and, when nsrc is set (H a multiple of kFDepth), leaves holding rows
+// 0 .. kFDepth-1 of the next item: the refill of slot d in the last period
+// is exactly the next item's row d. Without nsrc the tail refills re-read
+// the last row and the caller loads the next ring itself.
 template <int MT>
 __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int c0, int nsel,
-                                              int lane, const uint16_t* src, bool col_ok,
-                                              u32x4 (&ring)[kFDepth], const int* s_rows,
+                                              const char* src, uint32_t loff,
+                                              bool col_ok, const char* nsrc,
+                                              u32x4 (&ring)[kFDepth],
+                                              const int* s_rows,
                                               const uint16_t (*s_wxh)[kFMaxHW],
                                               const uint16_t (*s_wxl)[kFMaxHW],
-                                              const float (*s_wy)[kFRows], const float* s_inv) {
+                                              const float (*s_wy)[kFRows], const float* s_inv,
+                                              int lane_in) {
+  // the lane-derived LDS addresses are built here, per item, rather than
+  // hoisted out of the item loop and held live across it
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
   const int n16 = lane & 15, g4 = lane >> 4;
   // A: wx of row 16 h + n16 at columns 8 g4 .. 8 g4 + 7, hi and lo parts
   bf16x8 ahi[MT], alo[MT];
@@ -271,8 +327,12 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
       const int i = i0 + d;
       if (i < p.H) {
         const u32x4 v = col_ok ? ring[d] : u32x4{0u, 0u, 0u, 0u};
-        const int in = i + kFDepth < p.H ? i + kFDepth : p.H - 1;
-        ring[d] = *reinterpret_cast<const u32x4*>(src + (size_t)in * p.W);
+        const int ni = i + kFDepth;
+        const size_t rowb = (size_t)p.W * 2;
+        const char* a = ni < p.H ? src + ni * rowb
+                        : nsrc   ? nsrc + (ni - p.H) * rowb
+                                 : src + (p.H - 1) * rowb;
+        ring[d] = load_row(a, loff);
         const bf16x8 bv = __builtin_bit_cast(bf16x8, v);
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
@@ -299,7 +359,9 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
   }
 }
 
-__global__ __launch_bounds__(kFThreads, 2) void vkp_fast_kernel(VkFastParams p) {
+__global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_kernel(VkFastParams p) {
+  __shared__ int s_list[kFList];  // crop << 2 | row block
+  __shared__ int s_wsum[kFWaves];
   __shared__ int s_rows[kFRows];
   __shared__ uint8_t s_dummy0[kFRows], s_dummy1[kFRows];
   __shared__ int s_nvalid, s_nsel;
@@ -308,101 +370,160 @@ __global__ __launch_bounds__(kFThreads, 2) void vkp_fast_kernel(VkFastParams p) 
   __shared__ __align__(16) uint16_t s_wxh[kFRows][kFMaxHW];
   __shared__ __align__(16) uint16_t s_wxl[kFRows][kFMaxHW];
   __shared__ __align__(16) float s_wy[kFMaxHW][kFRows];
-  __shared__ float s_x[kFRows], s_y[kFRows], s_dx0[kFRows], s_dy0[kFRows], s_inv[kFRows];
+  __shared__ float s_inv[kFRows];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const ItemCoord ic = xcd_item(blockIdx.x, p.items_per_crop);
-  const int b = ic.crop;
-  if (b >= p.B) return;
-  const int rblk = ic.item / p.cblocks, cblk = ic.item - rblk * p.cblocks;
 
-  // the crop's masks and keypoints in one round trip, then rows from LDS
-  if (tid < p.R) {
-    const size_t o = (size_t)b * p.R + tid;
-    s_valid[tid] = p.valid[o];
-    s_kx[tid] = p.kpts[2 * o];
-    s_ky[tid] = p.kpts[2 * o + 1];
+  // (crop, row block) pairs with valid rows, in crop order: a crop with n
+  // valid rows has ceil(n / kFRows) row blocks (the split select_rows uses)
+  int nlist = 0;
+  for (int base = 0; base < p.B; base += kFThreads) {
+    const int bb = base + tid;
+    const int nb = bb < p.B ? (count_valid(p, bb) + kFRows - 1) / kFRows : 0;
+    int x = nb;  // inclusive scan over the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    lds_sync();
+    int first = nlist + x - nb;
+    for (int w = 0; w < kFWaves; ++w) {
+      const int s = s_wsum[w];
+      if (w < wave) first += s;
+      nlist += s;
+    }
+    for (int j = 0; j < nb; ++j) s_list[first + j] = (bb << 2) | j;
+    lds_sync();
   }
-  lds_sync();
-  if (wave == 0)
-    select_rows(s_valid, nullptr, p.R, lane, rblk, kFRows, s_rows, s_dummy0, s_dummy1, &s_nvalid,
-                &s_nsel);
-  lds_sync();
-  const int nsel = s_nsel;
-  if (nsel == 0) return;
-  const int MT = (nsel + 15) / 16;
+  const int nitems = nlist * p.cblocks;
+  int k = blockIdx.x;
+  if (k >= nitems) return;
 
-  // B of wave w: channel c0 + n16, image row i, columns 8 g4 .. 8 g4 + 7
-  // (lanes past the row's columns carry zeros). The first kFDepth rows are
-  // requested now, ahead of the weight set-up.
-  const int c0 = cblk * kFCh + 16 * wave;
-  const bool wave_on = c0 < p.C;
   const int g4 = lane >> 4;
   const bool col_ok = 8 * g4 < p.W;
-  const uint16_t* src =
-      p.support + ((size_t)b * p.C + (wave_on ? c0 : 0) + (lane & 15)) * p.S + (col_ok ? 8 * g4 : 0);
+  int b = 0, rblk = 0, c0 = 0;
+  auto decode = [&](int kk, int& bo, int& ro, int& co) {
+    const int e = kk / p.cblocks;
+    const int ent = __builtin_amdgcn_readfirstlane(s_list[e]);
+    bo = ent >> 2;
+    ro = ent & 3;
+    co = (kk - e * p.cblocks) * kFCh + 16 * wave;
+  };
+  decode(k, b, rblk, c0);
+  bool on = c0 < p.C;
+  const uint32_t loff =
+      (uint32_t)(((lane & 15) * p.S + (col_ok ? 8 * g4 : 0)) * 2);
+  const char* src = item_base(p, b, on ? c0 : 0);
+
+  // masks and keypoints of the item's crop (registers until staged)
+  uint8_t mv = 0;
+  float mx = 0.f, my = 0.f;
+  if (tid < p.R) {
+    const size_t o = (size_t)b * p.R + tid;
+    mv = p.valid[o];
+    mx = p.kpts[2 * o];
+    my = p.kpts[2 * o + 1];
+  }
   u32x4 ring[kFDepth];
-  if (wave_on) {
 #pragma unroll
-    for (int d = 0; d < kFDepth; ++d) {
-      const int i = d < p.H ? d : p.H - 1;
-      ring[d] = *reinterpret_cast<const u32x4*>(src + (size_t)i * p.W);
-    }
+  for (int d = 0; d < kFDepth; ++d) {
+    ring[d] = u32x4{0u, 0u, 0u, 0u};
+    if (on && d < p.H) ring[d] = load_row(src + (size_t)d * p.W * 2, loff);
   }
 
-  // per-row keypoint and nearest-centre offsets (rows past nsel: weight 0)
-  if (tid < kFRows) {
-    float x = 0.f, y = 0.f;
+  for (;;) {
+    // stage the crop's masks and keypoints, pick the item's rows
+    if (tid < p.R) {
+      s_valid[tid] = mv;
+      s_kx[tid] = mx;
+      s_ky[tid] = my;
+    }
+    lds_sync();
+    if (wave == 0)
+      select_rows(s_valid, nullptr, p.R, lane, rblk, kFRows, s_rows, s_dummy0, s_dummy1,
+                  &s_nvalid, &s_nsel);
+    lds_sync();
+    const int nsel = s_nsel;
+    // separable weight factors, each relative to the nearest cell centre
+    // (rows past nsel, and columns past W / H, get weight 0)
+#pragma nounroll
+    for (int q = tid; q < kFRows * kFMaxHW; q += kFThreads) {
+      const int m = q / kFMaxHW, j = q - m * kFMaxHW;
+      float wx = 0.f, wy = 0.f;
+      if (m < nsel) {
+        const int r = s_rows[m];
+        if (j < p.W) {
+          const float x = s_kx[r];
+          const float dx0 = nearest_centre_offset(x, p.stride, p.W);
+          const float d = ((float)j + 0.5f) * p.stride - x;
+          wx = expf(-(d * d - dx0 * dx0) * p.inv2s2);
+        }
+        if (j < p.H) {
+          const float y = s_ky[r];
+          const float dy0 = nearest_centre_offset(y, p.stride, p.H);
+          const float d = ((float)j + 0.5f) * p.stride - y;
+          wy = expf(-(d * d - dy0 * dy0) * p.inv2s2);
+        }
+      }
+      const uint16_t hi = f32_to_bf16_bits(wx);
+      s_wxh[m][j] = hi;
+      s_wxl[m][j] = f32_to_bf16_bits(wx - bf16_bits_to_f32(hi));
+      s_wy[j][m] = wy;
+    }
+    lds_sync();
+    // normaliser: sum_ij wy(i) wx(j) = (sum_i wy)(sum_j wx), with wx as the
+    // hi + lo parts the MFMA sees
     if (tid < nsel) {
-      x = s_kx[s_rows[tid]];
-      y = s_ky[s_rows[tid]];
+      float sx = 0.f, sy = 0.f;
+      for (int j = 0; j < p.W; ++j)
+        sx += bf16_bits_to_f32(s_wxh[tid][j]) + bf16_bits_to_f32(s_wxl[tid][j]);
+      for (int i = 0; i < p.H; ++i) sy += s_wy[i][tid];
+      s_inv[tid] = 1.f / (sx * sy);
     }
-    const float dx0 = nearest_centre_offset(x, p.stride, p.W);
-    const float dy0 = nearest_centre_offset(y, p.stride, p.H);
-    s_x[tid] = x;
-    s_y[tid] = y;
-    s_dx0[tid] = dx0 * dx0;
-    s_dy0[tid] = dy0 * dy0;
-  }
-  lds_sync();
-  // separable weight factors, each relative to the nearest cell centre
-  for (int q = tid; q < kFRows * kFMaxHW; q += kFThreads) {
-    const int m = q / kFMaxHW, j = q - m * kFMaxHW;
-    float wx = 0.f, wy = 0.f;
-    if (m < nsel) {
-      if (j < p.W) {
-        const float d = ((float)j + 0.5f) * p.stride - s_x[m];
-        wx = expf(-(d * d - s_dx0[m]) * p.inv2s2);
-      }
-      if (j < p.H) {
-        const float d = ((float)j + 0.5f) * p.stride - s_y[m];
-        wy = expf(-(d * d - s_dy0[m]) * p.inv2s2);
+    lds_sync();
+
+    // the next item: its masks and keypoints are requested now, its first
+    // rows by the last refills of this item's ring
+    const int kn = k + (int)gridDim.x;
+    const bool has_next = kn < nitems;
+    int bn = 0, rn = 0, cn = 0;
+    if (has_next) decode(kn, bn, rn, cn);
+    const bool on_n = has_next && cn < p.C;
+    const char* nsrc_all = on_n ? item_base(p, bn, cn) : nullptr;
+    const char* nsrc = p.chain ? nsrc_all : nullptr;
+    if (has_next && tid < p.R) {
+      const size_t o = (size_t)bn * p.R + tid;
+      mv = p.valid[o];
+      mx = p.kpts[2 * o];
+      my = p.kpts[2 * o + 1];
+    }
+    if (on) {
+      switch ((nsel + 15) / 16) {
+        case 1: vkp_fast_item<1>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
+        case 2: vkp_fast_item<2>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
+        case 3: vkp_fast_item<3>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
+        case 4: vkp_fast_item<4>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
+        default: vkp_fast_item<5>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
       }
     }
-    const uint16_t hi = f32_to_bf16_bits(wx);
-    s_wxh[m][j] = hi;
-    s_wxl[m][j] = f32_to_bf16_bits(wx - bf16_bits_to_f32(hi));
-    s_wy[j][m] = wy;
-  }
-  lds_sync();
-  // normaliser: sum_ij wy(i) wx(j) = (sum_i wy)(sum_j wx), with wx as the
-  // hi + lo parts the MFMA sees
-  if (tid < nsel) {
-    float sx = 0.f, sy = 0.f;
-    for (int j = 0; j < p.W; ++j)
-      sx += bf16_bits_to_f32(s_wxh[tid][j]) + bf16_bits_to_f32(s_wxl[tid][j]);
-    for (int i = 0; i < p.H; ++i) sy += s_wy[i][tid];
-    s_inv[tid] = 1.f / (sx * sy);
-  }
-  lds_sync();
-  if (!wave_on) return;
-  switch (MT) {
-    case 1: vkp_fast_item<1>(p, b, c0, nsel, lane, src, col_ok, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv); break;
-    case 2: vkp_fast_item<2>(p, b, c0, nsel, lane, src, col_ok, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv); break;
-    case 3: vkp_fast_item<3>(p, b, c0, nsel, lane, src, col_ok, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv); break;
-    case 4: vkp_fast_item<4>(p, b, c0, nsel, lane, src, col_ok, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv); break;
-    default: vkp_fast_item<5>(p, b, c0, nsel, lane, src, col_ok, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv); break;
+    if (on_n && !(on && p.chain)) {
+#pragma unroll
+      for (int d = 0; d < kFDepth; ++d)
+        if (d < p.H) ring[d] = load_row(nsrc_all + (size_t)d * p.W * 2, loff);
+    }
+    if (!has_next) break;
+    k = kn;
+    b = bn;
+    rblk = rn;
+    c0 = cn;
+    on = on_n;
+    src = on_n ? nsrc_all : src;
+    // every wave is done with this item's rows, weights and normaliser
+    // before the next set-up overwrites them
+    lds_sync();
   }
 }
 
@@ -418,25 +539,39 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
   if (a.bf16 && a.W <= kFMaxHW && a.H <= kFMaxHW && a.W % 8 == 0 && a.C % 16 == 0 &&
       a.R <= kFMaxR) {
     VkFastParams f;
-    f.support = static_cast<const uint16_t*>(a.support);
-    f.kpts = a.kpts;
-    f.valid = a.valid;
-    f.B = a.B;
     f.C = a.C;
     f.H = a.H;
     f.W = a.W;
     f.R = a.R;
     f.S = a.H * a.W;
+    f.chain = a.H % kFDepth == 0;
     f.stride = a.stride;
     f.inv2s2 = 1.f / (2.f * a.sigma * a.sigma);
-    f.protos = static_cast<uint16_t*>(a.protos);
     f.cblocks = (a.C + kFCh - 1) / kFCh;
-    f.items_per_crop = ((a.R + kFRows - 1) / kFRows) * f.cblocks;
-    const int crops_pad = (a.B + kXcds - 1) / kXcds * kXcds;
-    const long long grid = (long long)crops_pad * f.items_per_crop;
-    if (grid > INT_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(vkp_fast_kernel, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
-    return hipGetLastError();
+    f.mask_words = a.R % 4 == 0 && (reinterpret_cast<uintptr_t>(a.valid) & 3u) == 0;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int rblocks = (a.R + kFRows - 1) / kFRows;
+    const int crops_per_launch = kFList / rblocks;
+    // one launch per group of crops whose (crop, row block) list fits in LDS
+    for (int b0 = 0; b0 < a.B; b0 += crops_per_launch) {
+      const int nb = a.B - b0 < crops_per_launch ? a.B - b0 : crops_per_launch;
+      const size_t rows0 = (size_t)b0 * a.R;
+      f.support = static_cast<const uint16_t*>(a.support) + (size_t)b0 * a.C * f.S;
+      f.kpts = a.kpts + 2 * rows0;
+      f.valid = a.valid + rows0;
+      f.protos = static_cast<uint16_t*>(a.protos) + rows0 * a.C;
+      f.B = nb;
+      const long long items = (long long)nb * rblocks * f.cblocks;
+      const long long cap = (long long)kFWgPerCu * (cus > 0 ? cus : 1);
+      const int grid = (int)(items < cap ? items : cap);
+      hipLaunchKernelGGL(vkp_fast_kernel, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   VkParams p;
   p.support = a.support;
