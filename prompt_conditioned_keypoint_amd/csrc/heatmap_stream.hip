@@ -159,14 +159,15 @@ constexpr int kCWaves = 12;
 constexpr int kCThreads = kCWaves * kWave;  // 768
 constexpr int kKS = 32;                     // channels per K step (one MFMA K)
 constexpr int kMinStages = 3;               // LDS ring slots per item (loads run
-constexpr int kMaxStages = 6;               // stages - 1 steps ahead), as LDS allows
+constexpr int kMaxStages = 3;               // stages - 1 steps ahead), as LDS allows
 constexpr int kGroupPx = 48;                // one wave unit: 3 N tiles of 16 pixels
 constexpr int kItemRows = 80;               // valid rows per item
 constexpr int kMaxMH = kItemRows / 16;      // M tiles per modality
-constexpr int kMaxDualUnits = 3;            // wave units with both modalities (acc budget)
 constexpr int kMaxDma = 5;                  // direct-to-LDS loads per wave per stage
 constexpr int kRowSlots = 5;                // kernel row in LDS: 4 x 16 B + 1 pad slot
-constexpr int kVis = 1, kTxt = 2;
+// item modes: rows of one modality, or both modalities present, in which
+// case each row's two kernels enter as one pre-weighted combination
+constexpr int kVis = 1, kTxt = 2, kComb = 3;
 
 struct ContractParams {
   const uint16_t* query;
@@ -178,7 +179,6 @@ struct ContractParams {
   int ng;        // wave N groups per chunk (divides 12)
   int chunk_px;  // ng * 48
   int nchunks, rblocks, items_per_crop, nsteps;
-  int halves;       // 2: a dual-prompt block of more than 48 rows takes two passes
   int lds_bytes;    // dynamic LDS of the workgroup
   float* heat;
 };
@@ -300,7 +300,12 @@ struct ItemShape {
   bool has_v;
 };
 
-// K loop, row norms and epilogue for one item. MODE: modalities present;
+// K loop, row norms and epilogue for one item. MODE: kVis / kTxt (one
+// modality: the row norms are summed along the K loop and the fusion weight
+// is applied to the finished sums) or kComb (both modalities: each step's
+// kernel-row slice is first replaced in LDS by the weighted combination
+// w_v k_v + w_t k_t, as a bfloat16 hi part over the visual rows and a lo
+// part over the text rows, so a row needs one accumulator and two MFMAs).
 // UPW: wave units (one M tile x one 48-pixel group) a wave may own.
 template <int MODE, int UPW>
 __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned char* lds,
@@ -308,7 +313,8 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
                                               const ItemShape& it, int b, int wave, int lane,
                                               const int* s_rows, const uint8_t* s_mv,
                                               const uint8_t* s_mt, float (*s_w)[kItemRows]) {
-  constexpr int NM = (MODE == (kVis | kTxt)) ? 2 : 1;
+  constexpr bool COMB = MODE == kComb;
+  constexpr int NM = COMB ? 2 : 1;  // A operands per unit (hi + lo, or the one modality)
   const int tid = wave * kWave + lane;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int gw = wave % it.ng;           // this wave's pixel group
@@ -318,39 +324,44 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   const int row_bytes = it.rs * 16;
   const int arow0 = it.MH * 16;          // kernel rows per modality in LDS
 
-  bool on[NM][UPW];
+  // masked rows: zero A (one modality); in kComb their weights are 0
+  bool on[UPW];
 #pragma unroll
   for (int u = 0; u < UPW; ++u) {
     const int slot = 16 * (h0 + u * hstep) + n16;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      const bool vis = (MODE == kVis) || (MODE == (kVis | kTxt) && m == 0);
-      on[m][u] = slot < it.nsel && (vis ? s_mv[slot] : s_mt[slot]);
-    }
+    on[u] = COMB || (slot < it.nsel && (MODE == kVis ? s_mv[slot] : s_mt[slot]));
   }
-  f32x4 acc[UPW][NM][3];
+  f32x4 acc[UPW][3];
 #pragma unroll
   for (int u = 0; u < UPW; ++u)
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int t = 0; t < 3; ++t) acc[u][m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // row norms: thread 4 a + c sums the squares of 16-byte column c of
-  // staged kernel row a, step by step
-  const bool norm_thread = tid < 4 * it.arows;
+    for (int t = 0; t < 3; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // row norms (one modality): thread 4 a + c sums the squares of 16-byte
+  // column c of staged kernel row a, step by step
+  const bool norm_thread = !COMB && tid < 4 * it.arows;
   const int nrow = tid >> 2, ncol = tid & 3;
+  // combination (kComb): thread 4 a + c rewrites column c of row slot a;
+  // its weights are read once step 0 (and the weights' DMA before it) landed
+  const bool comb_thread = COMB && tid < 4 * arow0;
+  float wv = 0.f, wt = 0.f;
   float ss = 0.f;
 
   unsigned char* const aring = lds + (size_t)it.stages * it.fbytes;
   const int ahead = it.stages - 1;  // loads run this many steps ahead
   for (int k = 0; k < p.nsteps; ++k) {
-    if (k > 0) {
+    {
       // step k (features, then kernel rows) has landed for this wave once at
       // most the loads of the younger steps issued so far remain
       const int younger = min(ahead - 1, p.nsteps - 1 - k);
       wait_vmcnt_upto(younger * (pl.nf + pl.na));
     }
     lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
+    if constexpr (COMB) {
+      if (k == 0 && comb_thread && nrow < it.nsel) {
+        wv = s_w[0][nrow];
+        wt = s_w[1][nrow];
+      }
+    }
     if (k + ahead < p.nsteps) {
       const int slot = (k + ahead) % it.stages;
       issue_features(pl, bs, lds + (size_t)slot * it.fbytes, wave, k + ahead);
@@ -359,7 +370,33 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
 
     const int cur = k % it.stages;
     const unsigned char* sb = lds + (size_t)cur * it.fbytes;
-    const unsigned char* sa = aring + (size_t)cur * it.abytes;
+    unsigned char* const sa = aring + (size_t)cur * it.abytes;
+    if constexpr (COMB) {
+      if (comb_thread) {
+        u32x4* pv = reinterpret_cast<u32x4*>(sa + nrow * (kRowSlots * 16) + 16 * ncol);
+        u32x4* pt = reinterpret_cast<u32x4*>(sa + (arow0 + nrow) * (kRowSlots * 16) + 16 * ncol);
+        const u32x4 v = *pv, t = *pt;
+        u32x4 hi, lo;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t h2 = 0, l2 = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float x = fmaf(wt, bf16_bits_to_f32((t[d] >> (16 * e)) & 0xffffu),
+                                 wv * bf16_bits_to_f32((v[d] >> (16 * e)) & 0xffffu));
+            const uint32_t hb = f32_to_bf16_bits(x);
+            const uint32_t lb = f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
+            h2 |= hb << (16 * e);
+            l2 |= lb << (16 * e);
+          }
+          hi[d] = h2;
+          lo[d] = l2;
+        }
+        *pv = hi;
+        *pt = lo;
+      }
+      lds_barrier();  // the combined rows are in place
+    }
     // B: lane (n16, g4) of N tile t receives channels 8 g4 .. 8 g4 + 7 of
     // pixel gpx + 16 t + n16 from two transposing 8-byte reads (rows
     // 8 g4 + n16/4 and +4, columns 4 (n16 % 4) .. +3 of the tile)
@@ -392,10 +429,10 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
       for (int m = 0; m < NM; ++m) {
         const int ar = m * arow0 + 16 * h + n16;
         const u32x4 v = *reinterpret_cast<const u32x4*>(sa + ar * (kRowSlots * 16) + 16 * g4);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, on[m][u] ? v : u32x4{0u, 0u, 0u, 0u});
+        const bf16x8 a = __builtin_bit_cast(bf16x8, on[u] ? v : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
         for (int t = 0; t < 3; ++t)
-          acc[u][m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv[t], acc[u][m][t], 0, 0, 0);
+          acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv[t], acc[u][t], 0, 0, 0);
       }
     }
     if (norm_thread) {
@@ -408,20 +445,13 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
       }
     }
   }
-  // fusion weights mask / (n ||k||) from the norms
-  ss += __shfl_xor(ss, 1, kWave);
-  ss += __shfl_xor(ss, 2, kWave);
-  if (norm_thread && ncol == 0) {
-    const int mi = nrow / arow0, slot = nrow - mi * arow0;
-    const int mod = (it.has_v && mi == 0) ? 0 : 1;
-    if (slot < it.nsel) {
-      const bool on_row = mod == 0 ? s_mv[slot] : s_mt[slot];
-      float w = 0.f;
-      if (on_row) {
-        const float n = (float)((int)s_mv[slot] + (int)s_mt[slot]);
-        w = 1.f / (fmaxf(sqrtf(ss), 1e-12f) * n);
-      }
-      s_w[mod][slot] = w;
+  // fusion weights mask / (n ||k||) from the norms (one modality: n = 1)
+  if constexpr (!COMB) {
+    ss += __shfl_xor(ss, 1, kWave);
+    ss += __shfl_xor(ss, 2, kWave);
+    if (norm_thread && ncol == 0 && nrow < it.nsel) {
+      const bool on_row = MODE == kVis ? s_mv[nrow] : s_mt[nrow];
+      s_w[0][nrow] = on_row ? 1.f / fmaxf(sqrtf(ss), 1e-12f) : 0.f;
     }
   }
   lds_barrier();  // the ring is free; the weights are visible
@@ -444,14 +474,13 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
         const int slot = 16 * h + 4 * g4 + i;
         if (slot < base || slot >= base + rows_per_pass || slot >= it.nsel) continue;
         float* dst = Pl + (slot - base) * pitch + gpx + n16;
-        if constexpr (NM == 2) {
-          const float wv = s_w[0][slot], wt = s_w[1][slot];
+        if constexpr (COMB) {
 #pragma unroll
-          for (int t = 0; t < 3; ++t) dst[16 * t] = fmaf(wt, acc[u][1][t][i], wv * acc[u][0][t][i]);
+          for (int t = 0; t < 3; ++t) dst[16 * t] = acc[u][t][i];
         } else {
-          const float w = s_w[MODE == kVis ? 0 : 1][slot];
+          const float w = s_w[0][slot];
 #pragma unroll
-          for (int t = 0; t < 3; ++t) dst[16 * t] = w * acc[u][0][t][i];
+          for (int t = 0; t < 3; ++t) dst[16 * t] = w * acc[u][t][i];
         }
       }
     }
@@ -520,22 +549,28 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   it.MH = (it.nsel + 15) / 16;
   it.nmod = (int)has_v + (int)has_t;
   it.arows = it.nmod * it.MH * 16;
-  // both modalities over more than three M tiles would not fit the
-  // accumulators: such a block takes its chunk in two halves, one after the
-  // other (the features are still read once, the kernel rows twice). The
-  // grid holds no empty workgroups: an idle one still occupies a CU's LDS
-  // until dispatch moves on.
-  const bool split = p.halves == 2 && it.nmod == 2 && it.MH > kMaxDualUnits;
-  it.ng = split ? p.ng / 2 : p.ng;
+  it.ng = p.ng;
   it.chunk_px = it.ng * kGroupPx;
   it.rs = it.chunk_px / 8 + 1;
-#pragma nounroll
-  for (int half = 0; half < (split ? 2 : 1); ++half) {
-  // per-pass inputs are opaque, so nothing lane-dependent from one pass is
-  // kept alive for the next
+  it.px0 = chunk * p.chunk_px;
+  // both modalities: the fusion weights w = 1 / (n ||k||) of every row come
+  // from the row-norm pass, parked in the row's heatmap just past the H*W
+  // floats this kernel writes. They go straight to LDS ahead of the ring
+  // prologue (entry 64 j + lane of s_w from wave j), so the K loop's wait
+  // for step 0 covers them; slots past nsel are never read.
+  const bool comb = has_v && has_t;
+  if (comb && wave * kWave < 2 * kItemRows) {
+    const int e = wave * kWave + lane;
+    const int wm = e / kItemRows, wslot = e - wm * kItemRows;
+    if (e < 2 * kItemRows && wslot < it.nsel)
+      __builtin_amdgcn_global_load_lds(
+          (glb_void*)(p.heat + ((size_t)b * p.R + s_rows[wslot]) * ((size_t)16 * p.S) + p.S + wm),
+          (lds_void*)(&s_w[0][0] + wave * kWave), 4, 0, 0);
+  }
+  // a lane id the compiler cannot see through keeps the lane-dependent
+  // set-up below from being hoisted and held across the K loop
   int lane_p = lane;
   asm volatile("" : "+v"(lane_p));
-  it.px0 = chunk * p.chunk_px + half * it.chunk_px;
   const int nF = kKS * it.rs;                   // feature slots of a step
   const int nfi = (nF + kWave - 1) / kWave;     // feature blocks
   const int nA = it.arows * kRowSlots;          // kernel-row slots of a step
@@ -553,8 +588,9 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // 16-byte column u % rs (the last one pads the row); past the map: the
   // row's start. Kernel-row slot v < nA: kernel row (modality index,
   // slot) = v / 5, 16-byte column v % 5 (the fifth pads); masked or empty
-  // slots load the modality's first valid row and are zeroed before the
-  // MFMA. Everything else is a stand-in that is never read.
+  // slots load the modality's first valid row (finite) and are zeroed
+  // before the MFMA, or weighted by 0 in the combination. Everything else
+  // is a stand-in that is never read.
   DmaPlan pl;
   pl.nf = wave < nfi ? (nfi - wave + kCWaves - 1) / kCWaves : 0;
   pl.qa0 = (wave - nfi % kCWaves + kCWaves) % kCWaves;
@@ -594,18 +630,80 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
     issue_features(pl, bs, lds + (size_t)st * it.fbytes, wave, st);
     issue_rows(pl, bs, aring + (size_t)st * it.abytes, st);
   }
-  wait_vmcnt<0>();  // the prologue steps
 
   const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
   if (has_v && has_t)
-    contract_dispatch<kVis | kTxt, kMaxDualUnits>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows,
-                                                  s_mv, s_mt, s_w);
+    contract_dispatch<kComb, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+                                     s_w);
   else if (has_v)
     contract_dispatch<kVis, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                     s_w);
   else
     contract_dispatch<kTxt, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                     s_w);
+}
+
+// ---------------------------------------------------------------------------
+// row norms for the contraction's two-modality items
+// ---------------------------------------------------------------------------
+// One wave per (crop, row). In a crop that holds both modalities, every
+// valid row gets its two fusion weights w_m = mask_m / (n ||k_m||)
+// (||k|| clamped below at 1e-12, n = number of set masks), written to the
+// row's heatmap at floats H*W and H*W + 1: past the low-res map that the
+// contraction parks there, and overwritten by the expand pass.
+constexpr int kNWaves = 4;
+
+struct NormParams {
+  const uint16_t* kv;
+  const uint8_t* mv;
+  const uint16_t* kt;
+  const uint8_t* mt;
+  int B, C, R, S;
+  int groups_per_crop;  // ceil(R / kNWaves)
+  float* heat;
+};
+
+__device__ __forceinline__ float sum_squares8(u32x4 x) {
+  float s = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float lo = __uint_as_float(x[d] << 16), hi = __uint_as_float(x[d] & 0xffff0000u);
+    s = fmaf(lo, lo, s);
+    s = fmaf(hi, hi, s);
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(kNWaves * kWave) void row_norm_kernel(NormParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.x / p.groups_per_crop;
+  const int r = (blockIdx.x - b * p.groups_per_crop) * kNWaves + wave;
+  if (b >= p.B || r >= p.R) return;
+  const uint8_t* mv = p.mv + (size_t)b * p.R;
+  const uint8_t* mt = p.mt + (size_t)b * p.R;
+  bool av = false, at = false;
+  for (int base = 0; base < p.R; base += kWave) {
+    const int q = base + lane;
+    av = av || (q < p.R && mv[q]);
+    at = at || (q < p.R && mt[q]);
+  }
+  if (__ballot(av) == 0 || __ballot(at) == 0) return;
+  const bool v = mv[r] != 0, t = mt[r] != 0;
+  if (!v && !t) return;
+  const size_t row = ((size_t)b * p.R + r) * p.C;
+  float ssv = 0.f, sst = 0.f;
+  for (int c = 8 * lane; c < p.C; c += 8 * kWave) {
+    if (v) ssv += sum_squares8(*reinterpret_cast<const u32x4*>(p.kv + row + c));
+    if (t) sst += sum_squares8(*reinterpret_cast<const u32x4*>(p.kt + row + c));
+  }
+  ssv = wave_sum(ssv);
+  sst = wave_sum(sst);
+  if (lane == 0) {
+    const float n = (float)((int)v + (int)t);
+    float* h = p.heat + ((size_t)b * p.R + r) * ((size_t)16 * p.S) + p.S;
+    h[0] = v ? 1.f / (fmaxf(sqrtf(ssv), 1e-12f) * n) : 0.f;
+    h[1] = t ? 1.f / (fmaxf(sqrtf(sst), 1e-12f) * n) : 0.f;
   }
 }
 
@@ -709,9 +807,6 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
   sp.chunk_px = sp.ng * kGroupPx;
   sp.nchunks = ceil_div(S, sp.chunk_px);
   sp.rblocks = rblocks;
-  // a dual-prompt block with more than 3 M tiles needs ceil(MH * ng / 12)
-  // <= 3 wave units: true for ng <= 6; with ng = 12 it takes half chunks
-  sp.halves = sp.ng == 12 ? 2 : 1;
   // LDS of an item: three feature slots and five kernel-row slots
   int max_instr = 0;
   size_t max_lds = 0;
@@ -722,9 +817,8 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
     const size_t lds = (size_t)(kMinStages * nfi + kMinStages * nai) * 1024;
     if (lds > max_lds) max_lds = lds;
   };
-  need(sp.chunk_px, sp.halves == 2 ? 2 * 16 * kMaxDualUnits : 2 * kItemRows);
+  need(sp.chunk_px, 2 * kItemRows);
   need(sp.chunk_px, kItemRows);
-  if (sp.halves == 2) need(sp.chunk_px / 2, 2 * kItemRows);
   // one workgroup per CU whatever its LDS (registers decide that), so an
   // item may deepen its ring into the whole budget
   sp.contract_lds = max_lds <= kLdsBudget ? kLdsBudget : max_lds;
@@ -740,6 +834,26 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R);
   if (!sp.ok) return hipErrorInvalidConfiguration;
   const long long crops_pad = (long long)(a.B + kXcds - 1) / kXcds * kXcds;
+
+  if (a.kv != nullptr && a.kt != nullptr) {
+    NormParams np;
+    np.kv = static_cast<const uint16_t*>(a.kv);
+    np.mv = a.mv;
+    np.kt = static_cast<const uint16_t*>(a.kt);
+    np.mt = a.mt;
+    np.B = a.B;
+    np.C = a.C;
+    np.R = a.R;
+    np.S = S;
+    np.groups_per_crop = ceil_div(a.R, kNWaves);
+    np.heat = a.heat;
+    const long long ngrid = (long long)a.B * np.groups_per_crop;
+    if (ngrid > INT_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(row_norm_kernel, dim3((unsigned)ngrid), dim3(kNWaves * kWave), 0, stream,
+                       np);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   ContractParams cp;
   cp.query = static_cast<const uint16_t*>(a.query);
@@ -759,7 +873,6 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.rblocks = sp.rblocks;
   cp.items_per_crop = sp.nchunks * sp.rblocks;
   cp.nsteps = a.C / kKS;
-  cp.halves = sp.halves;
   cp.lds_bytes = (int)sp.contract_lds;
   cp.heat = a.heat;
   const long long cgrid = crops_pad * cp.items_per_crop;

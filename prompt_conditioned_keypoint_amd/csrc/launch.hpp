@@ -57,7 +57,7 @@ hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream);
 // workgroup, low-res maps parked in the heatmap rows), then expand + decode
 // (one wave per valid row)
 struct StreamPlan {
-  int ng = 0, chunk_px = 0, nchunks = 0, rblocks = 0, halves = 1, wpg = 0;
+  int ng = 0, chunk_px = 0, nchunks = 0, rblocks = 0, wpg = 0;
   size_t contract_lds = 0, expand_lds = 0;
   bool ok = false;
 };
