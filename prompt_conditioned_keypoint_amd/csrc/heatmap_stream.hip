@@ -682,20 +682,50 @@ __global__ __launch_bounds__(kNWaves * kWave) void row_norm_kernel(NormParams p)
   if (b >= p.B || r >= p.R) return;
   const uint8_t* mv = p.mv + (size_t)b * p.R;
   const uint8_t* mt = p.mt + (size_t)b * p.R;
-  bool av = false, at = false;
-  for (int base = 0; base < p.R; base += kWave) {
-    const int q = base + lane;
-    av = av || (q < p.R && mv[q]);
-    at = at || (q < p.R && mt[q]);
+  // one pass over the crop's masks gives both the crop scan and this row's
+  // own masks; blocks of 4 x 64 rows with clamped indices, so every load of
+  // a block is requested before the first wait
+  uint32_t av = 0, at = 0, vr = 0, tr = 0;
+  for (int base = 0; base < p.R; base += 4 * kWave) {
+    uint32_t x[4], y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = min(base + i * kWave + lane, p.R - 1);
+      x[i] = mv[q];
+      y[i] = mt[q];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      av |= x[i];
+      at |= y[i];
+      if (base + i * kWave + lane == r) {
+        vr = x[i];
+        tr = y[i];
+      }
+    }
   }
-  if (__ballot(av) == 0 || __ballot(at) == 0) return;
-  const bool v = mv[r] != 0, t = mt[r] != 0;
+  const bool v = __ballot(vr != 0) != 0, t = __ballot(tr != 0) != 0;
+  if (__ballot(av != 0) == 0 || __ballot(at != 0) == 0) return;
   if (!v && !t) return;
   const size_t row = ((size_t)b * p.R + r) * p.C;
+  const uint16_t* kvr = p.kv + row;
+  const uint16_t* ktr = p.kt + row;
+  // sum of squares of the row, blocks of 2 x 512 channels requested at once
   float ssv = 0.f, sst = 0.f;
-  for (int c = 8 * lane; c < p.C; c += 8 * kWave) {
-    if (v) ssv += sum_squares8(*reinterpret_cast<const u32x4*>(p.kv + row + c));
-    if (t) sst += sum_squares8(*reinterpret_cast<const u32x4*>(p.kt + row + c));
+  for (int c0 = 0; c0 < p.C; c0 += 16 * kWave) {
+    u32x4 a[2], e[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = c0 + 8 * (i * kWave + lane);
+      const bool in = c < p.C;
+      a[i] = (v && in) ? *reinterpret_cast<const u32x4*>(kvr + c) : u32x4{0u, 0u, 0u, 0u};
+      e[i] = (t && in) ? *reinterpret_cast<const u32x4*>(ktr + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ssv += sum_squares8(a[i]);
+      sst += sum_squares8(e[i]);
+    }
   }
   ssv = wave_sum(ssv);
   sst = wave_sum(sst);
