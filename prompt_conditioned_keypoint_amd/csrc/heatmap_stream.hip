@@ -239,6 +239,7 @@ enum : uint32_t { kSrcF = 0, kSrcV = 1, kSrcT = 2, kSrcJunk = 3 };
 struct DmaPlan {
   uint32_t off[kMaxDma];
   uint32_t kinds;  // 2 bits per instruction
+  uint32_t live;   // bit i: this lane loads in instruction i (lane 0 always)
   int nf;          // feature loads of this wave per step (instructions 0 .. nf-1)
   int na;          // kernel-row loads per step (instructions nf .. nf+na-1)
   int qa0;         // first kernel-row block of this wave
@@ -268,7 +269,7 @@ __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases
                                                unsigned char* fs, int wave, int step) {
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
-    if (i < pl.nf)
+    if (i < pl.nf && ((pl.live >> i) & 1u))
       __builtin_amdgcn_global_load_lds((glb_void*)dma_source(pl, bs, i, step),
                                        (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024),
                                        16, 0, 0);
@@ -279,7 +280,7 @@ __device__ __forceinline__ void issue_rows(const DmaPlan& pl, const DmaBases& bs
                                            unsigned char* as, int step) {
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
-    if (i >= pl.nf && i < pl.nf + pl.na)
+    if (i >= pl.nf && i < pl.nf + pl.na && ((pl.live >> i) & 1u))
       __builtin_amdgcn_global_load_lds(
           (glb_void*)dma_source(pl, bs, i, step),
           (lds_void*)(as + (size_t)(pl.qa0 + kCWaves * (i - pl.nf)) * 1024), 16, 0, 0);
@@ -589,13 +590,16 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // row's start. Kernel-row slot v < nA: kernel row (modality index,
   // slot) = v / 5, 16-byte column v % 5 (the fifth pads); masked or empty
   // slots load the modality's first valid row (finite) and are zeroed
-  // before the MFMA, or weighted by 0 in the combination. Everything else
-  // is a stand-in that is never read.
+  // before the MFMA, or weighted by 0 in the combination. Pad slots and
+  // slots past the plan are never read: their lanes issue no load, except
+  // lane 0 (a stand-in), so every wave still issues each instruction and
+  // the per-step load counts the K loop waits on hold.
   DmaPlan pl;
   pl.nf = wave < nfi ? (nfi - wave + kCWaves - 1) / kCWaves : 0;
   pl.qa0 = (wave - nfi % kCWaves + kCWaves) % kCWaves;
   pl.na = pl.qa0 < nai ? (nai - pl.qa0 + kCWaves - 1) / kCWaves : 0;
   pl.kinds = 0;
+  pl.live = 0;
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i) {
     uint32_t kind = kSrcJunk, off = 0;
@@ -604,12 +608,14 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
       if (u < nF) {
         const int r = u / it.rs, cc = u - r * it.rs;
         const int px = it.px0 + 8 * cc;
-        kind = kSrcF;
-        off = (uint32_t)(r * p.S + ((cc < it.rs - 1 && px < p.S) ? px : 0));
+        if (cc < it.rs - 1) {
+          kind = kSrcF;
+          off = (uint32_t)(r * p.S + (px < p.S ? px : 0));
+        }
       }
     } else if (i < pl.nf + pl.na) {
       const int v = (pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p;
-      if (v < nA) {
+      if (v < nA && v % kRowSlots < 4) {
         const int ar = v / kRowSlots, ac = v - ar * kRowSlots;
         const int mi = ar / (it.MH * 16), slot = ar - mi * (it.MH * 16);
         const bool vis = has_v && mi == 0;
@@ -621,6 +627,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
     }
     pl.off[i] = off;
     pl.kinds |= kind << (2 * i);
+    if (kind != kSrcJunk || lane_p == 0) pl.live |= 1u << i;
   }
   // as many ring slots as the workgroup's LDS holds, within [3, 6]
   it.stages = p.lds_bytes / (it.fbytes + it.abytes);
