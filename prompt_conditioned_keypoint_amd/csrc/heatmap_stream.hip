@@ -164,7 +164,9 @@ constexpr int kGroupPx = 48;                // one wave unit: 3 N tiles of 16 pi
 constexpr int kItemRows = 80;               // valid rows per item
 constexpr int kMaxMH = kItemRows / 16;      // M tiles per modality
 constexpr int kMaxDma = 5;                  // direct-to-LDS loads per wave per stage
-constexpr int kRowSlots = 5;                // kernel row in LDS: 4 x 16 B + 1 pad slot
+constexpr int kRowSlots = 9;                // kernel row in LDS: 8 x 16 B (two K steps) + 1 pad
+constexpr int kPairSlots = 2;               // kernel-row ring: two slots of two K steps each
+constexpr size_t kContractLds = 158 * 1024; // dynamic LDS of a contraction workgroup
 // item modes: rows of one modality, or both modalities present, in which
 // case each row's two kernels enter as one pre-weighted combination
 constexpr int kVis = 1, kTxt = 2, kComb = 3;
@@ -240,6 +242,8 @@ struct DmaPlan {
   uint32_t off[kMaxDma];
   uint32_t kinds;  // 2 bits per instruction
   uint32_t live;   // bit i: this lane loads in instruction i (lane 0 always)
+  uint32_t live1;  // the same for a pair that holds one K step only (odd step count)
+  uint32_t second; // bit i: this lane's slot holds the pair's second step
   int nf;          // feature loads of this wave per step (instructions 0 .. nf-1)
   int na;          // kernel-row loads per step (instructions nf .. nf+na-1)
   int qa0;         // first kernel-row block of this wave
@@ -275,14 +279,18 @@ __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases
                                        16, 0, 0);
 }
 
-// kernel-row blocks of one step into kernel-row slot as
+// kernel-row blocks of two K steps (step, step + 1; step even) into
+// kernel-row slot as; `last` when step + 1 is past the end
 __device__ __forceinline__ void issue_rows(const DmaPlan& pl, const DmaBases& bs,
-                                           unsigned char* as, int step) {
+                                           unsigned char* as, int step, bool last) {
+  const uint32_t live = last ? pl.live1 : pl.live;
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
-    if (i >= pl.nf && i < pl.nf + pl.na && ((pl.live >> i) & 1u))
+    if (i >= pl.nf && i < pl.nf + pl.na && ((live >> i) & 1u))
       __builtin_amdgcn_global_load_lds(
-          (glb_void*)dma_source(pl, bs, i, step),
+          // in a one-step pair, lane 0's stand-in for a second-step column
+          // loads the crop's first feature bytes instead of past the row
+          (glb_void*)(last && ((pl.second >> i) & 1u) ? (uint64_t)bs.F : dma_source(pl, bs, i, step)),
           (lds_void*)(as + (size_t)(pl.qa0 + kCWaves * (i - pl.nf)) * 1024), 16, 0, 0);
 }
 
@@ -341,9 +349,11 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   // column c of staged kernel row a, step by step
   const bool norm_thread = !COMB && tid < 4 * it.arows;
   const int nrow = tid >> 2, ncol = tid & 3;
-  // combination (kComb): thread 4 a + c rewrites column c of row slot a;
-  // its weights are read once step 0 (and the weights' DMA before it) landed
-  const bool comb_thread = COMB && tid < 4 * arow0;
+  // combination (kComb): thread 8 a + c rewrites bf16 columns 4 c .. 4 c + 3
+  // of row slot a; its weights are read once step 0 (and the weights' DMA
+  // before it) landed
+  const bool comb_thread = COMB && tid < 8 * arow0;
+  const int crow = tid >> 3, ccol = tid & 7;
   float wv = 0.f, wt = 0.f;
   float ss = 0.f;
 
@@ -351,47 +361,49 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   const int ahead = it.stages - 1;  // loads run this many steps ahead
   for (int k = 0; k < p.nsteps; ++k) {
     {
-      // step k (features, then kernel rows) has landed for this wave once at
-      // most the loads of the younger steps issued so far remain
-      const int younger = min(ahead - 1, p.nsteps - 1 - k);
-      wait_vmcnt_upto(younger * (pl.nf + pl.na));
+      // step k (features, and with an even step the kernel rows of it and
+      // the next) has landed for this wave once at most the loads of the
+      // younger steps issued so far remain
+      int younger = 0;
+      for (int s = k + 1; s < k + ahead && s < p.nsteps; ++s)
+        younger += pl.nf + ((s & 1) == 0 ? pl.na : 0);
+      wait_vmcnt_upto(younger);
     }
     lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
     if constexpr (COMB) {
-      if (k == 0 && comb_thread && nrow < it.nsel) {
-        wv = s_w[0][nrow];
-        wt = s_w[1][nrow];
+      if (k == 0 && comb_thread && crow < it.nsel) {
+        wv = s_w[0][crow];
+        wt = s_w[1][crow];
       }
     }
     if (k + ahead < p.nsteps) {
-      const int slot = (k + ahead) % it.stages;
-      issue_features(pl, bs, lds + (size_t)slot * it.fbytes, wave, k + ahead);
-      issue_rows(pl, bs, aring + (size_t)slot * it.abytes, k + ahead);
+      const int s = k + ahead;
+      issue_features(pl, bs, lds + (size_t)(s % it.stages) * it.fbytes, wave, s);
+      if ((s & 1) == 0)
+        issue_rows(pl, bs, aring + (size_t)((s >> 1) % kPairSlots) * it.abytes, s, s + 1 == p.nsteps);
     }
 
     const int cur = k % it.stages;
     const unsigned char* sb = lds + (size_t)cur * it.fbytes;
-    unsigned char* const sa = aring + (size_t)cur * it.abytes;
+    // this step's half (16-byte slots 4 (k & 1) .. + 3) of its pair's rows
+    unsigned char* const sa = aring + (size_t)((k >> 1) % kPairSlots) * it.abytes + 64 * (k & 1);
     if constexpr (COMB) {
       if (comb_thread) {
-        u32x4* pv = reinterpret_cast<u32x4*>(sa + nrow * (kRowSlots * 16) + 16 * ncol);
-        u32x4* pt = reinterpret_cast<u32x4*>(sa + (arow0 + nrow) * (kRowSlots * 16) + 16 * ncol);
-        const u32x4 v = *pv, t = *pt;
-        u32x4 hi, lo;
+        u32x2* pv = reinterpret_cast<u32x2*>(sa + crow * (kRowSlots * 16) + 8 * ccol);
+        u32x2* pt = reinterpret_cast<u32x2*>(sa + (arow0 + crow) * (kRowSlots * 16) + 8 * ccol);
+        const u32x2 v = *pv, t = *pt;
+        u32x2 hi, lo;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint32_t h2 = 0, l2 = 0;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float x = fmaf(wt, bf16_bits_to_f32((t[d] >> (16 * e)) & 0xffffu),
-                                 wv * bf16_bits_to_f32((v[d] >> (16 * e)) & 0xffffu));
-            const uint32_t hb = f32_to_bf16_bits(x);
-            const uint32_t lb = f32_to_bf16_bits(x - bf16_bits_to_f32(hb));
-            h2 |= hb << (16 * e);
-            l2 |= lb << (16 * e);
-          }
-          hi[d] = h2;
-          lo[d] = l2;
+        for (int d = 0; d < 2; ++d) {
+          // two channels per word, the lower one in the low half; each pair
+          // rounded to nearest even by one packed conversion
+          const f32x2 x = {fmaf(wt, __uint_as_float(t[d] << 16), wv * __uint_as_float(v[d] << 16)),
+                           fmaf(wt, __uint_as_float(t[d] & 0xffff0000u),
+                                wv * __uint_as_float(v[d] & 0xffff0000u))};
+          const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+          const f32x2 r = {x[0] - __uint_as_float(hb << 16), x[1] - __uint_as_float(hb & 0xffff0000u)};
+          hi[d] = hb;
+          lo[d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
         }
         *pv = hi;
         *pt = lo;
@@ -574,7 +586,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   asm volatile("" : "+v"(lane_p));
   const int nF = kKS * it.rs;                   // feature slots of a step
   const int nfi = (nF + kWave - 1) / kWave;     // feature blocks
-  const int nA = it.arows * kRowSlots;          // kernel-row slots of a step
+  const int nA = it.arows * kRowSlots;          // kernel-row slots of a step pair
   const int nai = (nA + kWave - 1) / kWave;     // kernel-row blocks
   it.fbytes = nfi * 1024;
   it.abytes = nai * 1024;
@@ -588,7 +600,8 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // ---- DMA plan. Feature slot u < nF: feature row r = u / rs (channel),
   // 16-byte column u % rs (the last one pads the row); past the map: the
   // row's start. Kernel-row slot v < nA: kernel row (modality index,
-  // slot) = v / 5, 16-byte column v % 5 (the fifth pads); masked or empty
+  // slot) = v / 9, 16-byte column v % 9 of the step pair (the ninth pads:
+  // a row's 64 channels of two steps are one 128-byte line); masked or empty
   // slots load the modality's first valid row (finite) and are zeroed
   // before the MFMA, or weighted by 0 in the combination. Pad slots and
   // slots past the plan are never read: their lanes issue no load, except
@@ -600,6 +613,8 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   pl.na = pl.qa0 < nai ? (nai - pl.qa0 + kCWaves - 1) / kCWaves : 0;
   pl.kinds = 0;
   pl.live = 0;
+  pl.live1 = 0;
+  pl.second = 0;
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i) {
     uint32_t kind = kSrcJunk, off = 0;
@@ -615,27 +630,36 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
       }
     } else if (i < pl.nf + pl.na) {
       const int v = (pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p;
-      if (v < nA && v % kRowSlots < 4) {
+      if (v < nA && v % kRowSlots < kRowSlots - 1) {
         const int ar = v / kRowSlots, ac = v - ar * kRowSlots;
         const int mi = ar / (it.MH * 16), slot = ar - mi * (it.MH * 16);
         const bool vis = has_v && mi == 0;
         const bool on = slot < it.nsel && (vis ? s_mv[slot] : s_mt[slot]);
         const int use = on ? slot : (vis ? first_v : first_t);
         kind = vis ? kSrcV : kSrcT;
-        off = (uint32_t)s_rows[use] * (uint32_t)p.C + (ac < 4 ? 8 * ac : 0);
+        off = (uint32_t)s_rows[use] * (uint32_t)p.C + 8 * ac;
       }
     }
     pl.off[i] = off;
     pl.kinds |= kind << (2 * i);
     if (kind != kSrcJunk || lane_p == 0) pl.live |= 1u << i;
+    // a last pair with one step: the second step's columns are not read
+    // (they would run past the row)
+    const bool second = i >= pl.nf && kind != kSrcJunk &&
+                        ((pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p) % kRowSlots >= 4;
+    if ((kind != kSrcJunk && !second) || lane_p == 0) pl.live1 |= 1u << i;
+    if (second) pl.second |= 1u << i;
   }
-  // as many ring slots as the workgroup's LDS holds, within [3, 6]
-  it.stages = p.lds_bytes / (it.fbytes + it.abytes);
-  it.stages = it.stages < kMinStages ? kMinStages : (it.stages > kMaxStages ? kMaxStages : it.stages);
+  // feature ring slots: as many as the LDS holds next to the two
+  // kernel-row pair slots, within [2, 3] (with two pair slots, the kernel
+  // rows may run at most two steps ahead)
+  it.stages = (p.lds_bytes - kPairSlots * it.abytes) / it.fbytes;
+  it.stages = it.stages < 2 ? 2 : (it.stages > kMaxStages ? kMaxStages : it.stages);
   unsigned char* const aring = lds + (size_t)it.stages * it.fbytes;
   for (int st = 0; st < it.stages - 1 && st < p.nsteps; ++st) {
     issue_features(pl, bs, lds + (size_t)st * it.fbytes, wave, st);
-    issue_rows(pl, bs, aring + (size_t)st * it.abytes, st);
+    if ((st & 1) == 0)
+      issue_rows(pl, bs, aring + (size_t)((st >> 1) % kPairSlots) * it.abytes, st, st + 1 == p.nsteps);
   }
 
   const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
@@ -844,24 +868,24 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
   sp.chunk_px = sp.ng * kGroupPx;
   sp.nchunks = ceil_div(S, sp.chunk_px);
   sp.rblocks = rblocks;
-  // LDS of an item: three feature slots and five kernel-row slots
+  // LDS of an item: three feature slots and two kernel-row pair slots
   int max_instr = 0;
   size_t max_lds = 0;
   auto need = [&](int chunk_px, int arows) {
     const int nfi = ceil_div(kKS * (chunk_px / 8 + 1), kWave);
     const int nai = ceil_div(arows * kRowSlots, kWave);
     if (nfi + nai > max_instr) max_instr = nfi + nai;
-    const size_t lds = (size_t)(kMinStages * nfi + kMinStages * nai) * 1024;
+    const size_t lds = (size_t)(kMinStages * nfi + kPairSlots * nai) * 1024;
     if (lds > max_lds) max_lds = lds;
   };
   need(sp.chunk_px, 2 * kItemRows);
   need(sp.chunk_px, kItemRows);
   // one workgroup per CU whatever its LDS (registers decide that), so an
   // item may deepen its ring into the whole budget
-  sp.contract_lds = max_lds <= kLdsBudget ? kLdsBudget : max_lds;
+  sp.contract_lds = max_lds <= kContractLds ? kContractLds : max_lds;
   sp.wpg = S <= 4096 ? kEWaves : 1;
   sp.expand_lds = (size_t)sp.wpg * S * sizeof(float);
-  sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kLdsBudget &&
+  sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kContractLds &&
           sp.expand_lds <= 64 * 1024;
   return sp;
 }
