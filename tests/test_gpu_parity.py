@@ -288,6 +288,40 @@ def test_ragged_shapes(gkd, ora, dtype, shape):
     check_protos(pv.float().cpu().numpy(), op, mv, dtype, np.abs(q).reshape(B, -1).max(1))
 
 
+@pytest.mark.parametrize("shape,p_valid", [
+    ((3, 48, 9, 8, 30), 0.6),      # H not a multiple of the row-ring depth; C < one block
+    ((2, 32, 5, 16, 12), 0.7),     # short maps, no cross-item prefetch
+    ((2, 16, 1, 8, 5), 1.0),       # a one-row map
+    ((2, 144, 8, 16, 10), 0.5),    # a partial channel block (one wave of eight)
+    ((1, 16, 32, 32, 6), 1.0),     # the largest map of the bf16 fast path
+    ((2, 32, 8, 8, 256), 0.8),     # R = 256: up to four row blocks per crop
+    ((4100, 16, 8, 8, 4), 0.5),    # more crops than one launch lists (two launches)
+    ((1030, 16, 8, 8, 256), 0.1),  # four row blocks per crop: 1024 crops per launch
+])
+def test_vkp_bf16_fast_path_shapes(gkd, ora, shape, p_valid):
+    """The persistent bf16 VKP kernel off the benchmark's shape: rings that do
+    not run on into the next item, idle waves, several row blocks, crops
+    without a visual prompt, and batches split over several launches."""
+    B, C, H, W, R = shape
+    rng = np.random.default_rng(B + C * 7 + H * 31 + W * 131 + R)
+    q = gkdsynth.round_bf16_f32(rng.standard_normal((B, C, H, W)).astype(np.float32))
+    mv = (rng.random((B, R)) < p_valid).astype(np.uint8)
+    mv[0, 0] = 1
+    if B > 1:
+        mv[1] = 0                    # a crop with no visual prompt
+    kp = rng.uniform(0, [W * 16, H * 16], size=(B, R, 2)).astype(np.float32)
+    print(f"[vkp-fast] {shape} valid={int(mv.sum())}", flush=True)
+    out = torch.empty((B, R, C), dtype=torch.int16, device="cuda").fill_(0x7FC1).view(
+        torch.bfloat16)
+    before = out.clone()
+    gkd.vkp_pool(dev_tensor(q, torch.bfloat16), dev_tensor(kp), dev_tensor(mv), out=out)
+    torch.cuda.synchronize()
+    op = ora.vkp_pool(q, kp, mv, 16.0, 14.0, dtype="bf16")
+    check_protos(out.float().cpu().numpy(), op, mv, "bf16", np.abs(q).reshape(B, -1).max(1))
+    inval = torch.from_numpy(mv == 0).cuda()
+    assert torch.equal(out[inval].view(torch.int16), before[inval].view(torch.int16))
+
+
 def test_empty_batch_and_no_prompt_crops(gkd):
     q = torch.zeros((0, 64, 24, 24), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((0, 80, 64), dtype=torch.bfloat16, device="cuda")
