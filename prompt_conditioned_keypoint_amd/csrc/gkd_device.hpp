@@ -97,35 +97,47 @@ __device__ __forceinline__ ItemCoord xcd_item(int wg, int items_per_crop) {
 // rows are split into nblk near-equal blocks by rank; block `blk` gets the
 // ranks [lo, hi). Writes the selected row ids to rows[0..hi-lo) and returns
 // (total valid count) in *n_valid. Runs on wave 0 only; the caller syncs.
+// The masks of the first 128 rows are requested together and held in
+// registers for both passes (one memory round trip for R <= 128).
 __device__ __forceinline__ void select_rows(const uint8_t* m0, const uint8_t* m1,
                                             int R, int lane, int blk,
                                             int rows_per_blk, int* rows,
                                             uint8_t* sel_m0, uint8_t* sel_m1,
                                             int* n_valid, int* n_sel) {
-  int total = 0;
-  for (int base = 0; base < R; base += kWave) {
-    const int r = base + lane;
-    const bool v = r < R && ((m0 && m0[r]) || (m1 && m1[r]));
-    total += __popcll(__ballot(v));
+  constexpr int kHeld = 2;  // 64-row blocks held in registers
+  uint32_t held[kHeld];     // bit 0: m0 set, bit 1: m1 set
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) {
+    const int r = i * kWave + lane;
+    const bool in = r < R;
+    held[i] = ((in && m0 && m0[r]) ? 1u : 0u) | ((in && m1 && m1[r]) ? 2u : 0u);
   }
+  auto load_flags = [&](int r) -> uint32_t {
+    return ((r < R && m0 && m0[r]) ? 1u : 0u) | ((r < R && m1 && m1[r]) ? 2u : 0u);
+  };
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) total += __popcll(__ballot(held[i] != 0));
+  for (int base = kHeld * kWave; base < R; base += kWave)
+    total += __popcll(__ballot(load_flags(base + lane) != 0));
   const int nb = (total + rows_per_blk - 1) / rows_per_blk;
   const int lo = nb ? (int)((long long)blk * total / nb) : 0;
   const int hi = nb ? (int)((long long)(blk + 1) * total / nb) : 0;
   int seen = 0;
-  for (int base = 0; base < R; base += kWave) {
-    const int r = base + lane;
-    const bool a = r < R && m0 && m0[r];
-    const bool t = r < R && m1 && m1[r];
-    const bool v = a || t;
+  auto place = [&](uint32_t f, int r) {
+    const bool v = f != 0;
     const uint64_t bal = __ballot(v);
     const int rank = seen + __popcll(bal & ((1ull << lane) - 1ull));
     if (v && rank >= lo && rank < hi) {
       rows[rank - lo] = r;
-      sel_m0[rank - lo] = a;
-      sel_m1[rank - lo] = t;
+      sel_m0[rank - lo] = f & 1u;
+      sel_m1[rank - lo] = (f >> 1) & 1u;
     }
     seen += __popcll(bal);
-  }
+  };
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) place(held[i], i * kWave + lane);
+  for (int base = kHeld * kWave; base < R; base += kWave) place(load_flags(base + lane), base + lane);
   if (lane == 0) {
     *n_valid = total;
     *n_sel = (blk < nb) ? hi - lo : 0;

@@ -1,5 +1,6 @@
-// heatmap_stream.hip - gkd_kernel_heatmap for bf16 features: two launches
-// on the caller's stream, each shaped for one side of the memory system.
+// heatmap_stream.hip - gkd_kernel_heatmap for bf16 features: up to three
+// launches on the caller's stream, each shaped for one side of the memory
+// system.
 //
 // The head (GKDT-L GGUF model card, section "Model": rows padded to 80
 // with masks, L2 kernel norm, 1x1 kernel conv against 4x bilinearly
@@ -8,13 +9,19 @@
 // argmax, so the contraction runs at the features' own resolution and only
 // its result is expanded.
 //
+// 0. row_prep_kernel (only when both prompt modalities are passed): for the
+//    rows of crops that hold both, the fusion weights and, by linearity of
+//    the per-row fusion, the single combined kernel w_v k_v + w_t k_t, split
+//    into bfloat16 hi and lo parts and parked in the row's own heatmap.
 // 1. contract_kernel (HBM reads): one workgroup per (crop, pixel chunk)
 //    takes ALL valid rows of the crop (up to 80 per item, both
 //    modalities), so every feature byte crosses HBM and the CU exactly
 //    once. Feature tiles [32 channels][chunk pixels] and the rows' kernel
-//    slices stream straight into a three-stage LDS ring
+//    slices stream straight into a three-slot LDS ring
 //    (global_load_lds_dwordx4); MFMA B operands come from transposing LDS
 //    reads (ds_read_b64_tr_b16), A operands from plain 16-byte LDS reads.
+//    Items with few kernel rows load one step ahead, the rest two, which
+//    evens out the items' finishing times under shared bandwidth.
 //    The fused low-resolution map of a row (float32, H*W values) is parked
 //    in the first H*W floats of that row's own heatmap.
 // 2. expand_kernel (HBM writes): one wave per valid row reads its parked
@@ -22,8 +29,8 @@
 //    non-temporal stores and reduces the first-occurrence argmax in
 //    registers. Waves are independent (no workgroup barrier), so a CU
 //    keeps many rows' stores in flight.
-// The parked maps are 1/16 of the heatmap bytes; they are read back before
-// the same wave overwrites them.
+// Everything parked in a heatmap row is read back before the expand pass
+// overwrites that row.
 #include "gkd_device.hpp"
 #include "launch.hpp"
 
@@ -158,8 +165,8 @@ __device__ __forceinline__ void write_keypoint(int32_t* idx, float* xy, float* s
 constexpr int kCWaves = 12;
 constexpr int kCThreads = kCWaves * kWave;  // 768
 constexpr int kKS = 32;                     // channels per K step (one MFMA K)
-constexpr int kMinStages = 3;               // LDS ring slots per item (loads run
-constexpr int kMaxStages = 3;               // stages - 1 steps ahead), as LDS allows
+constexpr int kStages = 3;                  // feature ring slots (loads run two steps ahead)
+constexpr int kLightArows = 32;             // items with at most this many kernel rows load one step ahead
 constexpr int kGroupPx = 48;                // one wave unit: 3 N tiles of 16 pixels
 constexpr int kItemRows = 80;               // valid rows per item
 constexpr int kMaxMH = kItemRows / 16;      // M tiles per modality
@@ -168,8 +175,28 @@ constexpr int kRowSlots = 9;                // kernel row in LDS: 8 x 16 B (two 
 constexpr int kPairSlots = 2;               // kernel-row ring: two slots of two K steps each
 constexpr size_t kContractLds = 158 * 1024; // dynamic LDS of a contraction workgroup
 // item modes: rows of one modality, or both modalities present, in which
-// case each row's two kernels enter as one pre-weighted combination
-constexpr int kVis = 1, kTxt = 2, kComb = 3;
+// case each row's two kernels enter as one pre-weighted combination, formed
+// either step by step in LDS (kComb) or once per row by the row pass, which
+// parks it in the row's own heatmap (kPre)
+constexpr int kVis = 1, kTxt = 2, kComb = 3, kPre = 4;
+
+// Where the row pass parks the combined kernel of a row (bfloat16 hi part,
+// then lo part, C values each) inside that row's heatmap: float offsets,
+// 128-byte aligned, past the H*W floats of the parked low-res map. Both are
+// 0 when a heatmap row is too short to hold them.
+struct CombLayout {
+  int hi = 0, lo = 0;
+};
+CombLayout comb_layout(int C, int S) {
+  CombLayout l;
+  const long long half = ((long long)C / 2 + 31) / 32 * 32;  // C bf16 in floats, rounded up
+  const long long hi = ((long long)S + 31) / 32 * 32;
+  if (hi + 2 * half <= 16LL * S) {
+    l.hi = (int)hi;
+    l.lo = (int)(hi + half);
+  }
+  return l;
+}
 
 struct ContractParams {
   const uint16_t* query;
@@ -182,6 +209,8 @@ struct ContractParams {
   int chunk_px;  // ng * 48
   int nchunks, rblocks, items_per_crop, nsteps;
   int lds_bytes;    // dynamic LDS of the workgroup
+  int comb_hi, comb_lo;  // CombLayout of the rows of two-modality crops (0: none)
+  int light_arows;       // items staging at most this many kernel rows load one step ahead
   float* heat;
 };
 
@@ -250,8 +279,8 @@ struct DmaPlan {
 };
 struct DmaBases {
   const uint16_t* F;   // the crop's feature map
-  const uint16_t* kv;  // the crop's visual kernel rows (or F)
-  const uint16_t* kt;  // the crop's text kernel rows (or F)
+  const uint16_t* kv;  // the crop's visual kernel rows, or combined hi parts (or F)
+  const uint16_t* kt;  // the crop's text kernel rows, or combined lo parts (or F)
   size_t fstep;        // feature elements per K step: 32 * S
 };
 
@@ -294,6 +323,20 @@ __device__ __forceinline__ void issue_rows(const DmaPlan& pl, const DmaBases& bs
           (lds_void*)(as + (size_t)(pl.qa0 + kCWaves * (i - pl.nf)) * 1024), 16, 0, 0);
 }
 
+// Two channels of the combination w_v k_v + w_t k_t (bf16 pairs, the lower
+// channel in the low half) split into a bfloat16 hi part and the bfloat16
+// rounding of the remainder, each pair rounded to nearest even by one
+// packed conversion. hi + lo carries about 16 significant bits.
+__device__ __forceinline__ void combine_pair(uint32_t v, uint32_t t, float wv, float wt,
+                                             uint32_t& hi, uint32_t& lo) {
+  const f32x2 x = {fmaf(wt, __uint_as_float(t << 16), wv * __uint_as_float(v << 16)),
+                   fmaf(wt, __uint_as_float(t & 0xffff0000u), wv * __uint_as_float(v & 0xffff0000u))};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  const f32x2 r = {x[0] - __uint_as_float(hb << 16), x[1] - __uint_as_float(hb & 0xffff0000u)};
+  hi = hb;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+}
+
 struct ItemShape {
   int ng;      // wave N groups of the item's chunk
   int chunk_px;
@@ -304,17 +347,19 @@ struct ItemShape {
   int arows;   // kernel rows staged per step: nmod * MH * 16
   int fbytes;  // feature slot (whole 1 KiB blocks)
   int abytes;  // kernel-row slot (whole 1 KiB blocks)
-  int stages;  // LDS ring slots
   int px0;     // first pixel of the chunk
   bool has_v;
+  int ahead;   // K steps the loads run ahead: 2, or 1 for light items
 };
 
 // K loop, row norms and epilogue for one item. MODE: kVis / kTxt (one
 // modality: the row norms are summed along the K loop and the fusion weight
-// is applied to the finished sums) or kComb (both modalities: each step's
+// is applied to the finished sums), kComb (both modalities: each step's
 // kernel-row slice is first replaced in LDS by the weighted combination
 // w_v k_v + w_t k_t, as a bfloat16 hi part over the visual rows and a lo
-// part over the text rows, so a row needs one accumulator and two MFMAs).
+// part over the text rows, so a row needs one accumulator and two MFMAs) or
+// kPre (the same hi and lo parts, formed once by the row pass and staged
+// directly).
 // UPW: wave units (one M tile x one 48-pixel group) a wave may own.
 template <int MODE, int UPW>
 __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned char* lds,
@@ -323,7 +368,8 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
                                               const int* s_rows, const uint8_t* s_mv,
                                               const uint8_t* s_mt, float (*s_w)[kItemRows]) {
   constexpr bool COMB = MODE == kComb;
-  constexpr int NM = COMB ? 2 : 1;  // A operands per unit (hi + lo, or the one modality)
+  constexpr bool TWO = COMB || MODE == kPre;  // rows carry hi and lo parts, weights applied
+  constexpr int NM = TWO ? 2 : 1;  // A operands per unit (hi + lo, or the one modality)
   const int tid = wave * kWave + lane;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int gw = wave % it.ng;           // this wave's pixel group
@@ -338,7 +384,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
 #pragma unroll
   for (int u = 0; u < UPW; ++u) {
     const int slot = 16 * (h0 + u * hstep) + n16;
-    on[u] = COMB || (slot < it.nsel && (MODE == kVis ? s_mv[slot] : s_mt[slot]));
+    on[u] = TWO || (slot < it.nsel && (MODE == kVis ? s_mv[slot] : s_mt[slot]));
   }
   f32x4 acc[UPW][3];
 #pragma unroll
@@ -347,7 +393,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     for (int t = 0; t < 3; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   // row norms (one modality): thread 4 a + c sums the squares of 16-byte
   // column c of staged kernel row a, step by step
-  const bool norm_thread = !COMB && tid < 4 * it.arows;
+  const bool norm_thread = !TWO && tid < 4 * it.arows;
   const int nrow = tid >> 2, ncol = tid & 3;
   // combination (kComb): thread 8 a + c rewrites bf16 columns 4 c .. 4 c + 3
   // of row slot a; its weights are read once step 0 (and the weights' DMA
@@ -357,16 +403,18 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   float wv = 0.f, wt = 0.f;
   float ss = 0.f;
 
-  unsigned char* const aring = lds + (size_t)it.stages * it.fbytes;
-  const int ahead = it.stages - 1;  // loads run this many steps ahead
+  unsigned char* const aring = lds + (size_t)kStages * it.fbytes;
+  const int ahead = it.ahead;  // loads run this many steps ahead
   for (int k = 0; k < p.nsteps; ++k) {
     {
       // step k (features, and with an even step the kernel rows of it and
       // the next) has landed for this wave once at most the loads of the
-      // younger steps issued so far remain
+      // younger steps issued so far remain; step 0's kernel rows were issued
+      // after the feature prologue, so step 0 waits for everything
       int younger = 0;
-      for (int s = k + 1; s < k + ahead && s < p.nsteps; ++s)
-        younger += pl.nf + ((s & 1) == 0 ? pl.na : 0);
+      if (k > 0)
+        for (int s = k + 1; s < k + ahead && s < p.nsteps; ++s)
+          younger += pl.nf + ((s & 1) == 0 ? pl.na : 0);
       wait_vmcnt_upto(younger);
     }
     lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
@@ -376,14 +424,15 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
         wt = s_w[1][crow];
       }
     }
+    // the loads of step k + ahead go to the slots step k - 1 used
     if (k + ahead < p.nsteps) {
       const int s = k + ahead;
-      issue_features(pl, bs, lds + (size_t)(s % it.stages) * it.fbytes, wave, s);
+      issue_features(pl, bs, lds + (size_t)(s % kStages) * it.fbytes, wave, s);
       if ((s & 1) == 0)
         issue_rows(pl, bs, aring + (size_t)((s >> 1) % kPairSlots) * it.abytes, s, s + 1 == p.nsteps);
     }
 
-    const int cur = k % it.stages;
+    const int cur = k % kStages;
     const unsigned char* sb = lds + (size_t)cur * it.fbytes;
     // this step's half (16-byte slots 4 (k & 1) .. + 3) of its pair's rows
     unsigned char* const sa = aring + (size_t)((k >> 1) % kPairSlots) * it.abytes + 64 * (k & 1);
@@ -395,15 +444,10 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
         u32x2 hi, lo;
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
-          // two channels per word, the lower one in the low half; each pair
-          // rounded to nearest even by one packed conversion
-          const f32x2 x = {fmaf(wt, __uint_as_float(t[d] << 16), wv * __uint_as_float(v[d] << 16)),
-                           fmaf(wt, __uint_as_float(t[d] & 0xffff0000u),
-                                wv * __uint_as_float(v[d] & 0xffff0000u))};
-          const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-          const f32x2 r = {x[0] - __uint_as_float(hb << 16), x[1] - __uint_as_float(hb & 0xffff0000u)};
-          hi[d] = hb;
-          lo[d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+          uint32_t h, l;
+          combine_pair(v[d], t[d], wv, wt, h, l);
+          hi[d] = h;
+          lo[d] = l;
         }
         *pv = hi;
         *pt = lo;
@@ -459,7 +503,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     }
   }
   // fusion weights mask / (n ||k||) from the norms (one modality: n = 1)
-  if constexpr (!COMB) {
+  if constexpr (!TWO) {
     ss += __shfl_xor(ss, 1, kWave);
     ss += __shfl_xor(ss, 2, kWave);
     if (norm_thread && ncol == 0 && nrow < it.nsel) {
@@ -487,7 +531,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
         const int slot = 16 * h + 4 * g4 + i;
         if (slot < base || slot >= base + rows_per_pass || slot >= it.nsel) continue;
         float* dst = Pl + (slot - base) * pitch + gpx + n16;
-        if constexpr (COMB) {
+        if constexpr (TWO) {
 #pragma unroll
           for (int t = 0; t < 3; ++t) dst[16 * t] = acc[u][t][i];
         } else {
@@ -546,33 +590,92 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   const uint8_t* mv = p.mv ? p.mv + (size_t)b * p.R : nullptr;
   const uint8_t* mt = p.mt ? p.mt + (size_t)b * p.R : nullptr;
 
-  if (wave == 0)
-    select_rows(mv, mt, p.R, lane, rblk, kItemRows, s_rows, s_mv, s_mt, &s_nvalid, &s_nsel);
-  __syncthreads();
+  // a lane id the compiler cannot see through keeps the lane-dependent
+  // set-up below from being hoisted and held across the K loop
+  int lane_p = lane;
+  asm volatile("" : "+v"(lane_p));
   ItemShape it;
-  it.nsel = s_nsel;
-  if (it.nsel == 0) return;
-  bool has_v = false, has_t = false;
-  int first_v = 0, first_t = 0;
-  for (int s = it.nsel - 1; s >= 0; --s) {
-    if (s_mv[s]) { has_v = true; first_v = s; }
-    if (s_mt[s]) { has_t = true; first_t = s; }
-  }
-  it.has_v = has_v;
-  it.MH = (it.nsel + 15) / 16;
-  it.nmod = (int)has_v + (int)has_t;
-  it.arows = it.nmod * it.MH * 16;
   it.ng = p.ng;
   it.chunk_px = it.ng * kGroupPx;
   it.rs = it.chunk_px / 8 + 1;
   it.px0 = chunk * p.chunk_px;
-  // both modalities: the fusion weights w = 1 / (n ||k||) of every row come
-  // from the row-norm pass, parked in the row's heatmap just past the H*W
-  // floats this kernel writes. They go straight to LDS ahead of the ring
-  // prologue (entry 64 j + lane of s_w from wave j), so the K loop's wait
-  // for step 0 covers them; slots past nsel are never read.
+  const int nF = kKS * it.rs;                   // feature slots of a step
+  const int nfi = (nF + kWave - 1) / kWave;     // feature blocks
+  it.fbytes = nfi * 1024;
+
+  DmaBases bs;
+  bs.F = p.query + (size_t)b * p.C * p.S;
+  bs.fstep = (size_t)kKS * p.S;
+  bs.kv = bs.F;
+  bs.kt = bs.F;
+
+  // ---- DMA plan, feature part. Feature slot u < nF: feature row r = u /
+  // rs (channel), 16-byte column u % rs (the last one pads the row); past
+  // the map: the row's start. Pad slots and slots past the plan are never
+  // read: their lanes issue no load, except lane 0 (a stand-in), so every
+  // wave still issues each instruction and the per-step load counts the K
+  // loop waits on hold. The feature prologue needs no row information, so
+  // it is in flight while the item's rows are selected.
+  DmaPlan pl;
+  pl.nf = wave < nfi ? (nfi - wave + kCWaves - 1) / kCWaves : 0;
+  pl.kinds = 0;
+  pl.live = 0;
+  pl.live1 = 0;
+  pl.second = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxDma; ++i) {
+    pl.off[i] = 0;
+    if (i >= pl.nf) continue;  // the kernel-row part sets its own bits below
+    uint32_t kind = kSrcJunk, off = 0;
+    const int u = (wave + kCWaves * i) * kWave + lane_p;
+    if (u < nF) {
+      const int r = u / it.rs, cc = u - r * it.rs;
+      const int px = it.px0 + 8 * cc;
+      if (cc < it.rs - 1) {
+        kind = kSrcF;
+        off = (uint32_t)(r * p.S + (px < p.S ? px : 0));
+      }
+    }
+    pl.off[i] = off;
+    pl.kinds |= kind << (2 * i);
+    if (kind != kSrcJunk || lane_p == 0) {
+      pl.live |= 1u << i;
+      pl.live1 |= 1u << i;
+    }
+  }
+  issue_features(pl, bs, lds, wave, 0);
+
+  if (wave == 0)
+    select_rows(mv, mt, p.R, lane, rblk, kItemRows, s_rows, s_mv, s_mt, &s_nvalid, &s_nsel);
+  __syncthreads();
+  it.nsel = s_nsel;
+  if (it.nsel == 0) {
+    wait_vmcnt<0>();  // the feature prologue lands before the LDS is released
+    return;
+  }
+  // modalities present and the first slot of each: every wave scans the
+  // item's slots (at most 80) with two ballots rather than a serial loop
+  static_assert(kItemRows <= 2 * kWave, "two ballots cover an item");
+  const uint64_t bv0 = __ballot(lane < it.nsel && s_mv[lane]);
+  const uint64_t bt0 = __ballot(lane < it.nsel && s_mt[lane]);
+  const uint64_t bv1 = __ballot(kWave + lane < it.nsel && s_mv[kWave + lane]);
+  const uint64_t bt1 = __ballot(kWave + lane < it.nsel && s_mt[kWave + lane]);
+  const bool has_v = (bv0 | bv1) != 0, has_t = (bt0 | bt1) != 0;
+  const int first_v = bv0 ? __builtin_ctzll(bv0) : (bv1 ? kWave + __builtin_ctzll(bv1) : 0);
+  const int first_t = bt0 ? __builtin_ctzll(bt0) : (bt1 ? kWave + __builtin_ctzll(bt1) : 0);
+  it.has_v = has_v;
+  it.MH = (it.nsel + 15) / 16;
+  it.nmod = (int)has_v + (int)has_t;
+  it.arows = it.nmod * it.MH * 16;
+  // both modalities: the row pass either parked each row's combined kernel
+  // in the row's heatmap (kPre) or parked the fusion weights w = 1 / (n
+  // ||k||) there, just past the H*W floats this kernel writes. The weights
+  // go straight to LDS ahead of the kernel-row prologue (entry 64 j + lane
+  // of s_w from wave j), so the K loop's wait for step 0 covers them; slots
+  // past nsel are never read.
   const bool comb = has_v && has_t;
-  if (comb && wave * kWave < 2 * kItemRows) {
+  const bool pre = comb && p.comb_hi > 0;
+  if (comb && !pre && wave * kWave < 2 * kItemRows) {
     const int e = wave * kWave + lane;
     const int wm = e / kItemRows, wslot = e - wm * kItemRows;
     if (e < 2 * kItemRows && wslot < it.nsel)
@@ -580,90 +683,68 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
           (glb_void*)(p.heat + ((size_t)b * p.R + s_rows[wslot]) * ((size_t)16 * p.S) + p.S + wm),
           (lds_void*)(&s_w[0][0] + wave * kWave), 4, 0, 0);
   }
-  // a lane id the compiler cannot see through keeps the lane-dependent
-  // set-up below from being hoisted and held across the K loop
-  int lane_p = lane;
-  asm volatile("" : "+v"(lane_p));
-  const int nF = kKS * it.rs;                   // feature slots of a step
-  const int nfi = (nF + kWave - 1) / kWave;     // feature blocks
   const int nA = it.arows * kRowSlots;          // kernel-row slots of a step pair
   const int nai = (nA + kWave - 1) / kWave;     // kernel-row blocks
-  it.fbytes = nfi * 1024;
   it.abytes = nai * 1024;
 
-  DmaBases bs;
-  bs.F = p.query + (size_t)b * p.C * p.S;
-  bs.fstep = (size_t)kKS * p.S;
-  bs.kv = has_v ? p.kv + (size_t)b * p.R * p.C : bs.F;
-  bs.kt = has_t ? p.kt + (size_t)b * p.R * p.C : bs.F;
+  // kernel rows: the prompt kernels (row pitch C), or the hi and lo parts
+  // parked in the crop's heatmap rows (row pitch 32 H*W bf16 values)
+  const uint16_t* const crop_heat =
+      reinterpret_cast<const uint16_t*>(p.heat + (size_t)b * p.R * 16 * p.S);
+  bs.kv = pre ? crop_heat + 2 * (size_t)p.comb_hi
+              : (has_v ? p.kv + (size_t)b * p.R * p.C : bs.F);
+  bs.kt = pre ? crop_heat + 2 * (size_t)p.comb_lo
+              : (has_t ? p.kt + (size_t)b * p.R * p.C : bs.F);
+  const uint32_t rpitch = pre ? 32u * (uint32_t)p.S : (uint32_t)p.C;
 
-  // ---- DMA plan. Feature slot u < nF: feature row r = u / rs (channel),
-  // 16-byte column u % rs (the last one pads the row); past the map: the
-  // row's start. Kernel-row slot v < nA: kernel row (modality index,
-  // slot) = v / 9, 16-byte column v % 9 of the step pair (the ninth pads:
-  // a row's 64 channels of two steps are one 128-byte line); masked or empty
-  // slots load the modality's first valid row (finite) and are zeroed
-  // before the MFMA, or weighted by 0 in the combination. Pad slots and
-  // slots past the plan are never read: their lanes issue no load, except
-  // lane 0 (a stand-in), so every wave still issues each instruction and
-  // the per-step load counts the K loop waits on hold.
-  DmaPlan pl;
-  pl.nf = wave < nfi ? (nfi - wave + kCWaves - 1) / kCWaves : 0;
+  // ---- DMA plan, kernel-row part. Kernel-row slot v < nA: kernel row
+  // (modality index, slot) = v / 9, 16-byte column v % 9 of the step pair
+  // (the ninth pads: a row's 64 channels of two steps are one 128-byte
+  // line); masked or empty slots load the modality's first valid row
+  // (finite) and are zeroed before the MFMA, or weighted by 0 in the
+  // combination (kPre: every slot below nsel holds a combination; empty ones
+  // load slot 0). Kernel-row blocks continue the feature blocks' round robin.
   pl.qa0 = (wave - nfi % kCWaves + kCWaves) % kCWaves;
   pl.na = pl.qa0 < nai ? (nai - pl.qa0 + kCWaves - 1) / kCWaves : 0;
-  pl.kinds = 0;
-  pl.live = 0;
-  pl.live1 = 0;
-  pl.second = 0;
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i) {
+    if (i < pl.nf || i >= pl.nf + pl.na) continue;
     uint32_t kind = kSrcJunk, off = 0;
-    if (i < pl.nf) {
-      const int u = (wave + kCWaves * i) * kWave + lane_p;
-      if (u < nF) {
-        const int r = u / it.rs, cc = u - r * it.rs;
-        const int px = it.px0 + 8 * cc;
-        if (cc < it.rs - 1) {
-          kind = kSrcF;
-          off = (uint32_t)(r * p.S + (px < p.S ? px : 0));
-        }
-      }
-    } else if (i < pl.nf + pl.na) {
-      const int v = (pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p;
-      if (v < nA && v % kRowSlots < kRowSlots - 1) {
-        const int ar = v / kRowSlots, ac = v - ar * kRowSlots;
-        const int mi = ar / (it.MH * 16), slot = ar - mi * (it.MH * 16);
-        const bool vis = has_v && mi == 0;
-        const bool on = slot < it.nsel && (vis ? s_mv[slot] : s_mt[slot]);
-        const int use = on ? slot : (vis ? first_v : first_t);
-        kind = vis ? kSrcV : kSrcT;
-        off = (uint32_t)s_rows[use] * (uint32_t)p.C + 8 * ac;
-      }
+    const int v = (pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p;
+    if (v < nA && v % kRowSlots < kRowSlots - 1) {
+      const int ar = v / kRowSlots, ac = v - ar * kRowSlots;
+      const int mi = ar / (it.MH * 16), slot = ar - mi * (it.MH * 16);
+      const bool vis = has_v && mi == 0;
+      const bool on = slot < it.nsel && (pre || (vis ? s_mv[slot] : s_mt[slot]));
+      const int use = on ? slot : (pre ? 0 : (vis ? first_v : first_t));
+      kind = vis ? kSrcV : kSrcT;
+      off = (uint32_t)s_rows[use] * rpitch + 8 * ac;
     }
     pl.off[i] = off;
     pl.kinds |= kind << (2 * i);
     if (kind != kSrcJunk || lane_p == 0) pl.live |= 1u << i;
     // a last pair with one step: the second step's columns are not read
     // (they would run past the row)
-    const bool second = i >= pl.nf && kind != kSrcJunk &&
-                        ((pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p) % kRowSlots >= 4;
+    const bool second = kind != kSrcJunk && v % kRowSlots >= 4;
     if ((kind != kSrcJunk && !second) || lane_p == 0) pl.live1 |= 1u << i;
     if (second) pl.second |= 1u << i;
   }
-  // feature ring slots: as many as the LDS holds next to the two
-  // kernel-row pair slots, within [2, 3] (with two pair slots, the kernel
-  // rows may run at most two steps ahead)
-  it.stages = (p.lds_bytes - kPairSlots * it.abytes) / it.fbytes;
-  it.stages = it.stages < 2 ? 2 : (it.stages > kMaxStages ? kMaxStages : it.stages);
-  unsigned char* const aring = lds + (size_t)it.stages * it.fbytes;
-  for (int st = 0; st < it.stages - 1 && st < p.nsteps; ++st) {
-    issue_features(pl, bs, lds + (size_t)st * it.fbytes, wave, st);
-    if ((st & 1) == 0)
-      issue_rows(pl, bs, aring + (size_t)((st >> 1) % kPairSlots) * it.abytes, st, st + 1 == p.nsteps);
-  }
+  // the rest of the prologue: features of step 1 (items that load two
+  // steps ahead), then the kernel rows of steps 0 and 1, so the K loop
+  // waits for everything at step 0. Items with few kernel rows move fewer
+  // bytes per step; loading them only one step ahead leaves the heavier
+  // items of the batch a larger share of the memory bandwidth, so all
+  // items finish closer together.
+  it.ahead = it.arows <= p.light_arows ? 1 : kStages - 1;
+  if (it.ahead > 1 && p.nsteps > 1) issue_features(pl, bs, lds + (size_t)it.fbytes, wave, 1);
+  unsigned char* const aring = lds + (size_t)kStages * it.fbytes;
+  issue_rows(pl, bs, aring, 0, p.nsteps == 1);
 
   const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
-  if (has_v && has_t)
+  if (pre)
+    contract_dispatch<kPre, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+                                    s_w);
+  else if (comb)
     contract_dispatch<kComb, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                      s_w);
   else if (has_v)
@@ -675,22 +756,26 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// row norms for the contraction's two-modality items
+// row pass for the contraction's two-modality items
 // ---------------------------------------------------------------------------
 // One wave per (crop, row). In a crop that holds both modalities, every
 // valid row gets its two fusion weights w_m = mask_m / (n ||k_m||)
-// (||k|| clamped below at 1e-12, n = number of set masks), written to the
-// row's heatmap at floats H*W and H*W + 1: past the low-res map that the
-// contraction parks there, and overwritten by the expand pass.
-constexpr int kNWaves = 4;
+// (||k|| clamped below at 1e-12, n = number of set masks) and, where its
+// heatmap row has room (CombLayout), the combination w_v k_v + w_t k_t as
+// bfloat16 hi and lo parts, parked there; otherwise the two weights are
+// parked at floats H*W and H*W + 1 for the contraction to combine step by
+// step. Either way the data lies past the low-res map that the contraction
+// parks in the row, and the expand pass overwrites it.
+constexpr int kPWaves = 4;
 
-struct NormParams {
+struct PrepParams {
   const uint16_t* kv;
   const uint8_t* mv;
   const uint16_t* kt;
   const uint8_t* mt;
   int B, C, R, S;
-  int groups_per_crop;  // ceil(R / kNWaves)
+  int groups_per_crop;  // ceil(R / kPWaves)
+  int comb_hi, comb_lo; // CombLayout (0: park the weights)
   float* heat;
 };
 
@@ -705,11 +790,11 @@ __device__ __forceinline__ float sum_squares8(u32x4 x) {
   return s;
 }
 
-__global__ __launch_bounds__(kNWaves * kWave) void row_norm_kernel(NormParams p) {
+__global__ __launch_bounds__(kPWaves * kWave) void row_prep_kernel(PrepParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x / p.groups_per_crop;
-  const int r = (blockIdx.x - b * p.groups_per_crop) * kNWaves + wave;
+  const int r = (blockIdx.x - b * p.groups_per_crop) * kPWaves + wave;
   if (b >= p.B || r >= p.R) return;
   const uint8_t* mv = p.mv + (size_t)b * p.R;
   const uint8_t* mt = p.mt + (size_t)b * p.R;
@@ -741,31 +826,60 @@ __global__ __launch_bounds__(kNWaves * kWave) void row_norm_kernel(NormParams p)
   const size_t row = ((size_t)b * p.R + r) * p.C;
   const uint16_t* kvr = p.kv + row;
   const uint16_t* ktr = p.kt + row;
-  // sum of squares of the row, blocks of 2 x 512 channels requested at once
-  float ssv = 0.f, sst = 0.f;
-  for (int c0 = 0; c0 < p.C; c0 += 16 * kWave) {
-    u32x4 a[2], e[2];
+  // the row's kernels in blocks of 512 channels (8 per lane); the first two
+  // blocks are requested together and stay in registers for the
+  // combination, the rest (C > 1024) are read again from cache
+  auto load8 = [&](const uint16_t* k, bool on, int c) -> u32x4 {
+    return (on && c < p.C) ? *reinterpret_cast<const u32x4*>(k + c) : u32x4{0u, 0u, 0u, 0u};
+  };
+  u32x4 a[2], e[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = c0 + 8 * (i * kWave + lane);
-      const bool in = c < p.C;
-      a[i] = (v && in) ? *reinterpret_cast<const u32x4*>(kvr + c) : u32x4{0u, 0u, 0u, 0u};
-      e[i] = (t && in) ? *reinterpret_cast<const u32x4*>(ktr + c) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ssv += sum_squares8(a[i]);
-      sst += sum_squares8(e[i]);
-    }
+  for (int i = 0; i < 2; ++i) {
+    a[i] = load8(kvr, v, 8 * (i * kWave + lane));
+    e[i] = load8(ktr, t, 8 * (i * kWave + lane));
+  }
+  float ssv = sum_squares8(a[0]) + sum_squares8(a[1]);
+  float sst = sum_squares8(e[0]) + sum_squares8(e[1]);
+  for (int c = 8 * (2 * kWave + lane); c < p.C; c += 8 * kWave) {
+    ssv += sum_squares8(load8(kvr, v, c));
+    sst += sum_squares8(load8(ktr, t, c));
   }
   ssv = wave_sum(ssv);
   sst = wave_sum(sst);
-  if (lane == 0) {
-    const float n = (float)((int)v + (int)t);
-    float* h = p.heat + ((size_t)b * p.R + r) * ((size_t)16 * p.S) + p.S;
-    h[0] = v ? 1.f / (fmaxf(sqrtf(ssv), 1e-12f) * n) : 0.f;
-    h[1] = t ? 1.f / (fmaxf(sqrtf(sst), 1e-12f) * n) : 0.f;
+  const float n = (float)((int)v + (int)t);
+  const float wv = v ? 1.f / (fmaxf(sqrtf(ssv), 1e-12f) * n) : 0.f;
+  const float wt = t ? 1.f / (fmaxf(sqrtf(sst), 1e-12f) * n) : 0.f;
+  float* h = p.heat + ((size_t)b * p.R + r) * ((size_t)16 * p.S);
+  if (p.comb_hi == 0) {
+    if (lane == 0) {
+      h[p.S] = wv;
+      h[p.S + 1] = wt;
+    }
+    return;
   }
+  // the combination, 8 channels per lane and block; an absent modality
+  // enters as zeros
+  uint16_t* const hr = reinterpret_cast<uint16_t*>(h + p.comb_hi);
+  uint16_t* const lr = reinterpret_cast<uint16_t*>(h + p.comb_lo);
+  auto store8 = [&](u32x4 x, u32x4 y, int c) {
+    u32x4 hi, lo;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t hd, ld;
+      combine_pair(x[d], y[d], wv, wt, hd, ld);
+      hi[d] = hd;
+      lo[d] = ld;
+    }
+    *reinterpret_cast<u32x4*>(hr + c) = hi;
+    *reinterpret_cast<u32x4*>(lr + c) = lo;
+  };
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = 8 * (i * kWave + lane);
+    if (c < p.C) store8(a[i], e[i], c);
+  }
+  for (int c = 8 * (2 * kWave + lane); c < p.C; c += 8 * kWave)
+    store8(load8(kvr, v, c), load8(ktr, t, c), c);
 }
 
 // ---------------------------------------------------------------------------
@@ -875,7 +989,7 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
     const int nfi = ceil_div(kKS * (chunk_px / 8 + 1), kWave);
     const int nai = ceil_div(arows * kRowSlots, kWave);
     if (nfi + nai > max_instr) max_instr = nfi + nai;
-    const size_t lds = (size_t)(kMinStages * nfi + kPairSlots * nai) * 1024;
+    const size_t lds = (size_t)(kStages * nfi + kPairSlots * nai) * 1024;
     if (lds > max_lds) max_lds = lds;
   };
   need(sp.chunk_px, 2 * kItemRows);
@@ -895,9 +1009,10 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R);
   if (!sp.ok) return hipErrorInvalidConfiguration;
   const long long crops_pad = (long long)(a.B + kXcds - 1) / kXcds * kXcds;
+  const CombLayout cl = comb_layout(a.C, S);
 
   if (a.kv != nullptr && a.kt != nullptr) {
-    NormParams np;
+    PrepParams np;
     np.kv = static_cast<const uint16_t*>(a.kv);
     np.mv = a.mv;
     np.kt = static_cast<const uint16_t*>(a.kt);
@@ -906,11 +1021,13 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
     np.C = a.C;
     np.R = a.R;
     np.S = S;
-    np.groups_per_crop = ceil_div(a.R, kNWaves);
+    np.groups_per_crop = ceil_div(a.R, kPWaves);
+    np.comb_hi = cl.hi;
+    np.comb_lo = cl.lo;
     np.heat = a.heat;
     const long long ngrid = (long long)a.B * np.groups_per_crop;
     if (ngrid > INT_MAX) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(row_norm_kernel, dim3((unsigned)ngrid), dim3(kNWaves * kWave), 0, stream,
+    hipLaunchKernelGGL(row_prep_kernel, dim3((unsigned)ngrid), dim3(kPWaves * kWave), 0, stream,
                        np);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -935,6 +1052,9 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.items_per_crop = sp.nchunks * sp.rblocks;
   cp.nsteps = a.C / kKS;
   cp.lds_bytes = (int)sp.contract_lds;
+  cp.comb_hi = (a.kv != nullptr && a.kt != nullptr) ? cl.hi : 0;
+  cp.comb_lo = (a.kv != nullptr && a.kt != nullptr) ? cl.lo : 0;
+  cp.light_arows = kLightArows;
   cp.heat = a.heat;
   const long long cgrid = crops_pad * cp.items_per_crop;
   if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;

@@ -246,14 +246,17 @@ def test_chain_vkp_heatmap_decode(gkd, ora):
 @pytest.mark.parametrize("shape", [(3, 40, 5, 7, 19), (2, 3, 1, 1, 4), (2, 72, 9, 10, 33),
                                    (5, 256, 24, 24, 80), (1, 1, 2, 3, 2), (3, 64, 8, 8, 16),
                                    (2, 96, 16, 16, 40), (9, 128, 24, 24, 37),
-                                   (2, 64, 32, 32, 8), (1, 32, 2, 72, 6), (2, 64, 8, 8, 200)])
+                                   (2, 64, 32, 32, 8), (1, 32, 2, 72, 6), (2, 64, 8, 8, 200),
+                                   (3, 256, 4, 4, 12)])
 def test_ragged_shapes(gkd, ora, dtype, shape):
     """Ragged channel counts, maps that do not fill a pixel chunk,
     degenerate 1x1 maps, random masks (dual, single, none). The bf16 shapes
     with C % 32 == 0 and H*W % 16 == 0 take the two-launch path
     (contraction + expand): several pixel chunks (32x32), rows wider than a
     wave (W = 72), more valid rows than one item holds (R = 200, up to four
-    row blocks), idle waves; the rest take the general kernel."""
+    row blocks), idle waves, heatmap rows too short to hold a two-prompt
+    row's combined kernel (4x4 maps with C = 256: combined step by step in
+    the contraction); the rest take the general kernel."""
     B, C, H, W, R = shape
     rng = np.random.default_rng(B * 1000 + C + H * 10 + W + R)
     q = rng.standard_normal((B, C, H, W)).astype(np.float32)
