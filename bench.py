@@ -160,8 +160,8 @@ def check_parity(d, heat_gpu, dec_gpu, ora_heat):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="longtail_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true")

@@ -230,7 +230,7 @@ constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;  // 512
 constexpr int kFRows = 80;                  // valid rows per item
 constexpr int kFMaxMT = kFRows / 16;
-constexpr int kFMaxHW = 32;                 // H, W <= 32
+constexpr int kFMaxHW = 32;                 // H, W <= 32 (one half wave per weight row)
 constexpr int kFCh = kFWaves * 16;          // channels per item
 constexpr int kFDepth = 4;                  // image rows loaded ahead per wave
 constexpr int kFMaxR = 256;                 // R <= 256 (masks and keypoints staged in LDS)
@@ -243,7 +243,8 @@ struct VkFastParams {
   const uint8_t* valid;
   int B, C, H, W, R, S;
   bool chain;  // H % kFDepth == 0: the ring runs on into the next item
-  float stride, inv2s2;
+  float stride, inv_stride;
+  float nl2s2;      // -log2(e) / (2 sigma^2): w = 2^(d^2 nl2s2)
   int cblocks;
   bool mask_words;  // R % 4 == 0 and the mask base 4-byte aligned
   uint16_t* protos;
@@ -256,6 +257,34 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Offset from x to the centre of the cell it falls in (clamped to the
+// grid), with the cell index from a product by 1 / stride: near a cell
+// border this may pick the neighbouring centre, which only changes the
+// common factor that the weighted mean divides out.
+__device__ __forceinline__ float centre_offset_fast(float x, float stride, float inv_stride, int n) {
+  int j = (int)floorf(x * inv_stride);
+  j = j < 0 ? 0 : (j > n - 1 ? n - 1 : j);
+  return ((float)j + 0.5f) * stride - x;
+}
+
+// Sum over each half wave (lanes 0-31, 32-63), complete in its last lane:
+// shifts by 1, 2, 4, 8 within each 16-lane row, then row 1 (3) adds the
+// total of row 0 (2) broadcast from its lane 15.
+__device__ __forceinline__ float dpp_add(float x, int v) { return x + __int_as_float(v); }
+__device__ __forceinline__ float half_wave_sum(float x) {
+  int v = __float_as_int(x);
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));  // row_shr:1
+  v = __float_as_int(x);
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));  // row_shr:2
+  v = __float_as_int(x);
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));  // row_shr:4
+  v = __float_as_int(x);
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));  // row_shr:8
+  v = __float_as_int(x);
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false)); // row_bcast:15
+  return x;
 }
 
 // Number of set mask bytes of one crop.
@@ -447,41 +476,40 @@ __global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_k
                   &s_nvalid, &s_nsel);
     lds_sync();
     const int nsel = s_nsel;
-    // separable weight factors, each relative to the nearest cell centre
-    // (rows past nsel, and columns past W / H, get weight 0)
+    // separable weight factors, each relative to the nearest cell centre,
+    // for the M tiles the MFMAs read (rows past nsel, and columns past
+    // W / H, get weight 0)
+    const int rows16 = (nsel + 15) / 16 * 16;
 #pragma nounroll
-    for (int q = tid; q < kFRows * kFMaxHW; q += kFThreads) {
+    for (int q = tid; q < rows16 * kFMaxHW; q += kFThreads) {
       const int m = q / kFMaxHW, j = q - m * kFMaxHW;
       float wx = 0.f, wy = 0.f;
       if (m < nsel) {
         const int r = s_rows[m];
         if (j < p.W) {
           const float x = s_kx[r];
-          const float dx0 = nearest_centre_offset(x, p.stride, p.W);
+          const float dx0 = centre_offset_fast(x, p.stride, p.inv_stride, p.W);
           const float d = ((float)j + 0.5f) * p.stride - x;
-          wx = expf(-(d * d - dx0 * dx0) * p.inv2s2);
+          wx = __builtin_amdgcn_exp2f((d * d - dx0 * dx0) * p.nl2s2);
         }
         if (j < p.H) {
           const float y = s_ky[r];
-          const float dy0 = nearest_centre_offset(y, p.stride, p.H);
+          const float dy0 = centre_offset_fast(y, p.stride, p.inv_stride, p.H);
           const float d = ((float)j + 0.5f) * p.stride - y;
-          wy = expf(-(d * d - dy0 * dy0) * p.inv2s2);
+          wy = __builtin_amdgcn_exp2f((d * d - dy0 * dy0) * p.nl2s2);
         }
       }
       const uint16_t hi = f32_to_bf16_bits(wx);
+      const uint16_t lo = f32_to_bf16_bits(wx - bf16_bits_to_f32(hi));
       s_wxh[m][j] = hi;
-      s_wxl[m][j] = f32_to_bf16_bits(wx - bf16_bits_to_f32(hi));
+      s_wxl[m][j] = lo;
       s_wy[j][m] = wy;
-    }
-    lds_sync();
-    // normaliser: sum_ij wy(i) wx(j) = (sum_i wy)(sum_j wx), with wx as the
-    // hi + lo parts the MFMA sees
-    if (tid < nsel) {
-      float sx = 0.f, sy = 0.f;
-      for (int j = 0; j < p.W; ++j)
-        sx += bf16_bits_to_f32(s_wxh[tid][j]) + bf16_bits_to_f32(s_wxl[tid][j]);
-      for (int i = 0; i < p.H; ++i) sy += s_wy[i][tid];
-      s_inv[tid] = 1.f / (sx * sy);
+      // normaliser: sum_ij wy(i) wx(j) = (sum_i wy)(sum_j wx), with wx as
+      // the hi + lo parts the MFMA sees; the 32 lanes of row m (a half
+      // wave: kFMaxHW = 32 and q steps by whole waves) sum in registers
+      const float sx = half_wave_sum(bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo));
+      const float sy = half_wave_sum(wy);
+      if (j == kFMaxHW - 1 && m < nsel) s_inv[m] = 1.f / (sx * sy);
     }
     lds_sync();
 
@@ -546,7 +574,8 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
     f.S = a.H * a.W;
     f.chain = a.H % kFDepth == 0;
     f.stride = a.stride;
-    f.inv2s2 = 1.f / (2.f * a.sigma * a.sigma);
+    f.inv_stride = 1.f / a.stride;
+    f.nl2s2 = (float)(-1.4426950408889634 / (2.0 * (double)a.sigma * (double)a.sigma));
     f.cblocks = (a.C + kFCh - 1) / kFCh;
     f.mask_words = a.R % 4 == 0 && (reinterpret_cast<uintptr_t>(a.valid) & 3u) == 0;
     int dev = 0, cus = 0;
