@@ -870,8 +870,10 @@ __global__ __launch_bounds__(kPWaves * kWave) void row_prep_kernel(PrepParams p)
       hi[d] = hd;
       lo[d] = ld;
     }
-    *reinterpret_cast<u32x4*>(hr + c) = hi;
-    *reinterpret_cast<u32x4*>(lr + c) = lo;
+    // non-temporal: the parts go out to memory now instead of staying dirty
+    // in L2 until the contraction's feature stream evicts them
+    __builtin_nontemporal_store(hi, reinterpret_cast<u32x4*>(hr + c));
+    __builtin_nontemporal_store(lo, reinterpret_cast<u32x4*>(lr + c));
   };
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
