@@ -297,6 +297,11 @@ __device__ __forceinline__ uint64_t dma_source(const DmaPlan& pl, const DmaBases
   return ((kind & 2u) ? hi : lo) + 2ull * pl.off[i];
 }
 
+// cache policy of the feature loads: non-temporal (each feature byte is
+// read once, so the stream should not displace what the next passes reuse
+// from L2 and the memory-side cache)
+constexpr int kFeatureCpol = 2;
+
 // feature blocks of one step into feature slot fs
 __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases& bs,
                                                unsigned char* fs, int wave, int step) {
@@ -305,7 +310,7 @@ __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases
     if (i < pl.nf && ((pl.live >> i) & 1u))
       __builtin_amdgcn_global_load_lds((glb_void*)dma_source(pl, bs, i, step),
                                        (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024),
-                                       16, 0, 0);
+                                       16, 0, kFeatureCpol);
 }
 
 // kernel-row blocks of two K steps (step, step + 1; step even) into
