@@ -42,6 +42,43 @@ HEATMAP_SRCS = [os.path.join(CSRC, n) for n in
                 ("heatmap.hip", "heatmap_stream.hip", "gkd_device.hpp", "launch.hpp")]
 
 
+class TimingEvent:
+    """A HIP timing event recorded on torch's current stream, created with
+    hipEventDisableSystemFence: recording it writes a timestamp without the
+    system-scope release (cache write-back) of a default event, which would
+    otherwise add to every step it brackets. Read with hipEventElapsedTime."""
+    _hip = None
+
+    def __init__(self, torch):
+        import ctypes
+        if TimingEvent._hip is None:
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._ct = ctypes
+        self._torch = torch
+        self.h = ctypes.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.h),
+                                                     ctypes.c_uint(0x20000000))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        stream = self._ct.c_void_p(self._torch.cuda.current_stream().cuda_stream)
+        rc = TimingEvent._hip.hipEventRecord(self.h, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        ms = self._ct.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.h:
+            TimingEvent._hip.hipEventDestroy(self.h)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -228,10 +265,9 @@ def main():
 
     # timed region: K whole steps, wall clock between two synchronisations
     log(f"[bench] timing {args.steps} steps")
-    # (two events per step, around the heatmap call only: every recorded
-    # event adds to the step)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-           for _ in range(args.steps)]
+    # (two events per step, around the heatmap call only, on the stream it
+    # is launched on; every recorded event adds a little to the step)
+    evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -241,7 +277,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     hm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     # the VKP launch duration, from a separate pass of a few steps
-    evv = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    evv = [[TimingEvent(torch) for _ in range(2)] for _ in range(5)]
     for k in range(5):
         step(ev_vkp=evv[k])
     torch.cuda.synchronize()
