@@ -208,7 +208,6 @@ struct ContractParams {
   int ng;        // wave N groups per chunk (divides 12)
   int chunk_px;  // ng * 48
   int nchunks, rblocks, items_per_crop, nsteps;
-  int lds_bytes;    // dynamic LDS of the workgroup
   int comb_hi, comb_lo;  // CombLayout of the rows of two-modality crops (0: none)
   int light_arows;       // items staging at most this many kernel rows load one step ahead
   float* heat;
@@ -518,44 +517,26 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   }
   lds_barrier();  // the ring is free; the weights are visible
 
-  // fused low-res maps -> LDS rows (passes of up to rows_per_pass) -> the
-  // first H*W floats of each row's heatmap with 16-byte stores. Lane
-  // (n16, g4) holds rows 4 g4 + i of each M tile at pixel 16 t + n16.
-  float* Pl = reinterpret_cast<float*>(lds);
-  const int pitch = it.chunk_px + 4;
-  const int rows_per_pass = p.lds_bytes / (pitch * 4);
-  const int q4 = it.chunk_px / 4;
+  // fused low-res maps -> the first H*W floats of each row's heatmap,
+  // straight from the accumulators: lane (n16, g4) holds rows 4 g4 + i of
+  // each M tile at pixel 16 t + n16, so 16 lanes store 64 contiguous bytes
+  // (no LDS staging and no barriers: an 80-row item's write-back no longer
+  // waits on passes through the LDS, which held at most 69 rows at a time)
   const size_t hw_out = (size_t)16 * p.S;
-  for (int base = 0; base < it.nsel; base += rows_per_pass) {
 #pragma unroll
-    for (int u = 0; u < UPW; ++u) {
-      const int h = h0 + u * hstep;
-      if (h >= it.MH) break;
+  for (int u = 0; u < UPW; ++u) {
+    const int h = h0 + u * hstep;
+    if (h >= it.MH) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int slot = 16 * h + 4 * g4 + i;
-        if (slot < base || slot >= base + rows_per_pass || slot >= it.nsel) continue;
-        float* dst = Pl + (slot - base) * pitch + gpx + n16;
-        if constexpr (TWO) {
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 16 * h + 4 * g4 + i;
+      if (slot >= it.nsel) continue;
+      const float w = TWO ? 1.f : s_w[0][slot];
+      float* dst = p.heat + ((size_t)b * p.R + s_rows[slot]) * hw_out + it.px0 + gpx + n16;
 #pragma unroll
-          for (int t = 0; t < 3; ++t) dst[16 * t] = acc[u][t][i];
-        } else {
-          const float w = s_w[0][slot];
-#pragma unroll
-          for (int t = 0; t < 3; ++t) dst[16 * t] = w * acc[u][t][i];
-        }
-      }
+      for (int t = 0; t < 3; ++t)
+        if (it.px0 + gpx + 16 * t + n16 < p.S) dst[16 * t] = TWO ? acc[u][t][i] : w * acc[u][t][i];
     }
-    lds_barrier();
-    const int nrows = min(rows_per_pass, it.nsel - base);
-    for (int e = tid; e < nrows * q4; e += kCThreads) {
-      const int r = e / q4, c4 = e - r * q4;
-      const int px = it.px0 + 4 * c4;
-      if (px < p.S)
-        *reinterpret_cast<f32x4*>(p.heat + ((size_t)b * p.R + s_rows[base + r]) * hw_out + px) =
-            *reinterpret_cast<const f32x4*>(Pl + r * pitch + 4 * c4);
-    }
-    lds_barrier();
   }
 }
 
@@ -1058,7 +1039,6 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.rblocks = sp.rblocks;
   cp.items_per_crop = sp.nchunks * sp.rblocks;
   cp.nsteps = a.C / kKS;
-  cp.lds_bytes = (int)sp.contract_lds;
   cp.comb_hi = (a.kv != nullptr && a.kt != nullptr) ? cl.hi : 0;
   cp.comb_lo = (a.kv != nullptr && a.kt != nullptr) ? cl.lo : 0;
   cp.light_arows = kLightArows;
