@@ -32,7 +32,12 @@
  *   - B == 0 or R == 0 is an empty batch: GKD_OK, nothing launched.
  *   - Every element count (e.g. B*R*4H*4W) must be below 2^31.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
- *   - `flags` is reserved and must be 0 (else GKD_ERR_UNSUPPORTED).
+ *   - `flags` must be 0 (else GKD_ERR_UNSUPPORTED), except for the
+ *     heatmap output format flag of gkd_kernel_heatmap (GKD_HEATMAP_BF16).
+ *
+ * ABI history: version 1 had float32 heatmaps only; version 2 adds
+ * GKD_HEATMAP_BF16 (gkd_kernel_heatmap's heatmaps argument became void *,
+ * which existing callers pass unchanged).
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -44,7 +49,11 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 1
+#define GKD_ABI_VERSION 2
+
+/* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
+ * (half the bytes of the dominant output stream). */
+#define GKD_HEATMAP_BF16 0x1u
 
 #ifndef GKD_API
 #define GKD_API __attribute__((visibility("default")))
@@ -130,7 +139,11 @@ GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
  *   kern_txt   [B,R,C]   dtype   text kernels; mask_txt [B,R] uint8.
  *                                Both NULL = no text prompt in the batch.
  *                                At least one modality must be given.
- *   heatmaps   [B,R,4H,4W] float32 output
+ *   heatmaps   [B,R,4H,4W] output: float32, or with flags = GKD_HEATMAP_BF16
+ *                                bfloat16 (each value rounded to nearest even
+ *                                from its float32 result). The fused decode
+ *                                takes the peak and score from the float32
+ *                                values in both formats.
  *   peak_idx   [B,R]   int32     optional fused decode (see gkd_peak_decode);
  *   peak_xy    [B,R,2] float32   all three NULL = no decode, else all three
  *   peak_score [B,R]   float32   non-NULL. Rows with no mask get the sentinel.
@@ -140,7 +153,7 @@ GKD_API gkd_status gkd_kernel_heatmap(const void *query, const void *kern_vis,
                               const uint8_t *mask_vis, const void *kern_txt,
                               const uint8_t *mask_txt, int B, int C, int H,
                               int W, int R, gkd_dtype dtype, uint32_t flags,
-                              float *heatmaps, int32_t *peak_idx,
+                              void *heatmaps, int32_t *peak_idx,
                               float *peak_xy, float *peak_score,
                               hipStream_t stream);
 

@@ -17,6 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
+GKD_ABI_VERSION = 2          # include/gkdhead.h
+GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
 STATUS = {0: "GKD_OK", 1: "GKD_ERR_NULL", 2: "GKD_ERR_SHAPE", 3: "GKD_ERR_DTYPE",
           4: "GKD_ERR_VALUE", 5: "GKD_ERR_UNSUPPORTED", 6: "GKD_ERR_HIP",
           7: "GKD_ERR_ALIGN"}
@@ -55,7 +57,7 @@ def load():
                                        _U32, _P, _P, _P, _P, _P]
     lib.gkd_peak_decode.restype = _I
     lib.gkd_peak_decode.argtypes = [_P, _P, _I, _I, _I, _I, _U32, _P, _P, _P, _P]
-    if lib.gkd_abi_version() != 1:
+    if lib.gkd_abi_version() != GKD_ABI_VERSION:
         raise ImportError("libgkdhead ABI version mismatch")
     _lib = lib
     return lib
@@ -120,13 +122,15 @@ def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
 
 
 def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=None,
-                   mask_txt=None, decode: bool = True, out=None, out_decode=None):
+                   mask_txt=None, decode: bool = True, out=None, out_decode=None,
+                   heat_dtype=torch.float32):
     """query [B,C,H,W] (f32|bf16); kern_* [B,R,C] in the query dtype with
     mask_* [B,R] u8 (None = modality absent).
 
-    Returns heatmaps [B,R,4H,4W] f32 and, if decode, (idx [B,R] i32,
-    xy [B,R,2] f32, score [B,R] f32). Rows with no mask set are not written
-    (they keep whatever `out` held)."""
+    Returns heatmaps [B,R,4H,4W] in heat_dtype (float32, or bfloat16 via
+    the GKD_HEATMAP_BF16 flag) and, if decode, (idx [B,R] i32, xy [B,R,2]
+    f32, score [B,R] f32). Rows with no mask set are not written (they keep
+    whatever `out` held)."""
     lib = load()
     _dev(query, "query", ndim=4)
     B, C, H, W = query.shape
@@ -143,9 +147,12 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
                 raise ValueError(f"kern_{name} must be [B,R,C], mask_{name} [B,R]")
     if R is None:
         raise ValueError("at least one prompt modality is required")
+    if heat_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"heat_dtype must be float32 or bfloat16, got {heat_dtype}")
+    flags = GKD_HEATMAP_BF16 if heat_dtype == torch.bfloat16 else 0
     if out is None:
-        out = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.float32, device=query.device)
-    _dev(out, "out", torch.float32)
+        out = torch.empty((B, R, 4 * H, 4 * W), dtype=heat_dtype, device=query.device)
+    _dev(out, "out", heat_dtype)
     if out.shape != (B, R, 4 * H, 4 * W):
         raise ValueError("out must be [B,R,4H,4W]")
     idx = xy = score = None
@@ -158,7 +165,7 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
             idx, xy, score = out_decode
     _check(lib.gkd_kernel_heatmap(_ptr(query), _ptr(kern_vis), _ptr(mask_vis),
                                   _ptr(kern_txt), _ptr(mask_txt), B, C, H, W, R,
-                                  _dtype_code(query), 0, _ptr(out), _ptr(idx), _ptr(xy),
+                                  _dtype_code(query), flags, _ptr(out), _ptr(idx), _ptr(xy),
                                   _ptr(score), _stream(query.device)))
     if decode:
         return out, (idx, xy, score)

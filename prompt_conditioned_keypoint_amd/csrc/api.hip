@@ -99,9 +99,10 @@ gkd_status gkd_vkp_pool(const void* support, const float* kpts_px, const uint8_t
 gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uint8_t* mask_vis,
                               const void* kern_txt, const uint8_t* mask_txt, int B, int C,
                               int H, int W, int R, gkd_dtype dtype, uint32_t flags,
-                              float* heatmaps, int32_t* peak_idx, float* peak_xy,
+                              void* heatmaps, int32_t* peak_idx, float* peak_xy,
                               float* peak_score, hipStream_t stream) {
-  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: flags must be 0");
+  if ((flags & ~(uint32_t)GKD_HEATMAP_BF16) != 0)
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: unknown flags 0x%x", (unsigned)flags);
   if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
     return fail(GKD_ERR_DTYPE, "gkd_kernel_heatmap: unknown dtype %d", (int)dtype);
   if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1)
@@ -150,6 +151,7 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   a.R = R;
   a.bf16 = dtype == GKD_DTYPE_BF16;
   a.heat = heatmaps;
+  a.heat_bf16 = (flags & GKD_HEATMAP_BF16) != 0;
   a.idx = peak_idx;
   a.xy = peak_xy;
   a.score = peak_score;

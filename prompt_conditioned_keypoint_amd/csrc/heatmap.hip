@@ -54,7 +54,8 @@ struct HmParams {
   int rows_per_item;  // <= kMT
   int items_per_crop;
   int nsteps;         // K steps: ceil(C / 32) for bf16, ceil(C / 16) for f32
-  float* heat;
+  void* heat;      // [B,R,4H,4W] float32, or bfloat16 when heat_bf16
+  bool heat_bf16;
   int32_t* idx;
   float* xy;
   float* score;
@@ -367,7 +368,7 @@ void heatmap_kernel(HmParams p) {
   const int Ho = 4 * p.H, Wo = 4 * p.W;
   for (int s = 0; s < nsel; ++s) {
     const float* Pr = P + (size_t)s * p.S;
-    float* out = p.heat + ((size_t)b * p.R + s_rows[s]) * (size_t)Ho * Wo;
+    const size_t out_e = ((size_t)b * p.R + s_rows[s]) * (size_t)Ho * Wo;  // row's first element
     float bv = -INFINITY;
     int bi = INT_MAX;
     for (int cell = tid; cell < p.S; cell += kThreads) {
@@ -389,7 +390,16 @@ void heatmap_kernel(HmParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = fmaf(yh[d], hi[e], yl[d] * lo[e]);
         const int y = 4 * i + d;
-        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out + (size_t)y * Wo + 4 * j));
+        const size_t e = out_e + (size_t)y * Wo + 4 * j;
+        if (p.heat_bf16) {
+          // round to nearest even; the peak below still uses the float32 values
+          const u32x2 v = {
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[0], o[1]}, bf16x2)),
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[2], o[3]}, bf16x2))};
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.heat) + e));
+        } else {
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(static_cast<float*>(p.heat) + e));
+        }
         const int base = y * Wo + 4 * j;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -468,6 +478,7 @@ hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream) {
   p.R = a.R;
   p.S = a.H * a.W;
   p.heat = a.heat;
+  p.heat_bf16 = a.heat_bf16;
   p.idx = a.idx;
   p.xy = a.xy;
   p.score = a.score;

@@ -105,20 +105,34 @@ struct RowGeom {
 // rows, so every output of a later cell has a larger flat index than any
 // output of an earlier one; the lane keeps (best value, its cell) with a
 // strict > and finds the position inside the cell once, at the end.
-template <bool SMALLW>
-__device__ __forceinline__ void expand_row(const float* P, float* out, const RowGeom& g, int lane,
-                                           bool decode, float& best_v, int& best_i) {
+// BF16: the row is stored as bfloat16 (each value rounded to nearest even
+// from the float32 result; the peak is still taken on the float32 values).
+template <bool SMALLW, bool BF16>
+__device__ __forceinline__ void expand_row(const float* P, void* out_row, const RowGeom& g,
+                                           int lane, bool decode, float& best_v, int& best_i) {
   float bv = -INFINITY;
   int bi = INT_MAX;  // SMALLW: best cell; otherwise best flat index
   for (int c = lane; c < g.S; c += kWave) {
     const int i = (int)(((uint64_t)(uint32_t)c * g.magic_w) >> 32), j = c - i * g.W;
     float o[16];
     cell_values(P, i, j, g.H, g.W, o);
-    float* dst = out + (size_t)(4 * i) * g.Wo + 4 * j;
+    const size_t e0 = (size_t)(4 * i) * g.Wo + 4 * j;  // element of output (4i, 4j)
+    if constexpr (BF16) {
+      uint16_t* dst = static_cast<uint16_t*>(out_row) + e0;
 #pragma unroll
-    for (int d = 0; d < 4; ++d)
-      __builtin_nontemporal_store(f32x4{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]},
-                                  reinterpret_cast<f32x4*>(dst + (size_t)d * g.Wo));
+      for (int d = 0; d < 4; ++d) {
+        const u32x2 v = {
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[4 * d], o[4 * d + 1]}, bf16x2)),
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[4 * d + 2], o[4 * d + 3]}, bf16x2))};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(dst + (size_t)d * g.Wo));
+      }
+    } else {
+      float* dst = static_cast<float*>(out_row) + e0;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        __builtin_nontemporal_store(f32x4{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]},
+                                    reinterpret_cast<f32x4*>(dst + (size_t)d * g.Wo));
+    }
     const float m = max16(o);
     if (SMALLW) {
       if (m > bv) {
@@ -183,15 +197,16 @@ constexpr int kVis = 1, kTxt = 2, kComb = 3, kPre = 4;
 // Where the row pass parks the combined kernel of a row (bfloat16 hi part,
 // then lo part, C values each) inside that row's heatmap: float offsets,
 // 128-byte aligned, past the H*W floats of the parked low-res map. Both are
-// 0 when a heatmap row is too short to hold them.
+// 0 when a heatmap row (row_f floats: 16 H*W for float32 heatmaps, 8 H*W
+// for bfloat16 ones) is too short to hold them.
 struct CombLayout {
   int hi = 0, lo = 0;
 };
-CombLayout comb_layout(int C, int S) {
+CombLayout comb_layout(int C, int S, long long row_f) {
   CombLayout l;
   const long long half = ((long long)C / 2 + 31) / 32 * 32;  // C bf16 in floats, rounded up
   const long long hi = ((long long)S + 31) / 32 * 32;
-  if (hi + 2 * half <= 16LL * S) {
+  if (hi + 2 * half <= row_f) {
     l.hi = (int)hi;
     l.lo = (int)(hi + half);
   }
@@ -210,7 +225,8 @@ struct ContractParams {
   int nchunks, rblocks, items_per_crop, nsteps;
   int comb_hi, comb_lo;  // CombLayout of the rows of two-modality crops (0: none)
   int light_arows;       // items staging at most this many kernel rows load one step ahead
-  float* heat;
+  float* heat;           // heatmap rows, viewed as floats (parking space)
+  size_t row_f;          // floats per heatmap row: 16 H*W (float32) or 8 H*W (bfloat16)
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 layout:
@@ -522,7 +538,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   // each M tile at pixel 16 t + n16, so 16 lanes store 64 contiguous bytes
   // (no LDS staging and no barriers: an 80-row item's write-back no longer
   // waits on passes through the LDS, which held at most 69 rows at a time)
-  const size_t hw_out = (size_t)16 * p.S;
+  const size_t hw_out = p.row_f;
 #pragma unroll
   for (int u = 0; u < UPW; ++u) {
     const int h = h0 + u * hstep;
@@ -666,7 +682,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
     const int wm = e / kItemRows, wslot = e - wm * kItemRows;
     if (e < 2 * kItemRows && wslot < it.nsel)
       __builtin_amdgcn_global_load_lds(
-          (glb_void*)(p.heat + ((size_t)b * p.R + s_rows[wslot]) * ((size_t)16 * p.S) + p.S + wm),
+          (glb_void*)(p.heat + ((size_t)b * p.R + s_rows[wslot]) * p.row_f + p.S + wm),
           (lds_void*)(&s_w[0][0] + wave * kWave), 4, 0, 0);
   }
   const int nA = it.arows * kRowSlots;          // kernel-row slots of a step pair
@@ -674,14 +690,14 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   it.abytes = nai * 1024;
 
   // kernel rows: the prompt kernels (row pitch C), or the hi and lo parts
-  // parked in the crop's heatmap rows (row pitch 32 H*W bf16 values)
+  // parked in the crop's heatmap rows (row pitch 2 row_f bf16 values)
   const uint16_t* const crop_heat =
-      reinterpret_cast<const uint16_t*>(p.heat + (size_t)b * p.R * 16 * p.S);
+      reinterpret_cast<const uint16_t*>(p.heat + (size_t)b * p.R * p.row_f);
   bs.kv = pre ? crop_heat + 2 * (size_t)p.comb_hi
               : (has_v ? p.kv + (size_t)b * p.R * p.C : bs.F);
   bs.kt = pre ? crop_heat + 2 * (size_t)p.comb_lo
               : (has_t ? p.kt + (size_t)b * p.R * p.C : bs.F);
-  const uint32_t rpitch = pre ? 32u * (uint32_t)p.S : (uint32_t)p.C;
+  const uint32_t rpitch = pre ? 2u * (uint32_t)p.row_f : (uint32_t)p.C;
 
   // ---- DMA plan, kernel-row part. Kernel-row slot v < nA: kernel row
   // (modality index, slot) = v / 9, 16-byte column v % 9 of the step pair
@@ -763,6 +779,7 @@ struct PrepParams {
   int groups_per_crop;  // ceil(R / kPWaves)
   int comb_hi, comb_lo; // CombLayout (0: park the weights)
   float* heat;
+  size_t row_f;         // floats per heatmap row
 };
 
 __device__ __forceinline__ float sum_squares8(u32x4 x) {
@@ -835,7 +852,7 @@ __global__ __launch_bounds__(kPWaves * kWave) void row_prep_kernel(PrepParams p)
   const float n = (float)((int)v + (int)t);
   const float wv = v ? 1.f / (fmaxf(sqrtf(ssv), 1e-12f) * n) : 0.f;
   const float wt = t ? 1.f / (fmaxf(sqrtf(sst), 1e-12f) * n) : 0.f;
-  float* h = p.heat + ((size_t)b * p.R + r) * ((size_t)16 * p.S);
+  float* h = p.heat + ((size_t)b * p.R + r) * p.row_f;
   if (p.comb_hi == 0) {
     if (lane == 0) {
       h[p.S] = wv;
@@ -883,14 +900,15 @@ struct ExpandParams {
   int wpg;               // rows (waves) per workgroup
   int groups_per_crop;   // ceil(R / wpg)
   uint64_t magic_w;      // ceil(2^32 / W)
-  float* heat;
+  float* heat;           // heatmap rows viewed as floats (the parked maps)
+  size_t row_f;          // floats per heatmap row
   int32_t* idx;
   float* xy;
   float* score;
 };
 
 // One wave per valid row of the crop (by rank).
-template <bool SMALLW>
+template <bool SMALLW, bool BF16>
 __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   extern __shared__ __align__(16) float lds_p[];
   const int lane = threadIdx.x & 63;
@@ -931,8 +949,7 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   }
   if (row < 0) return;
 
-  const size_t hw_out = (size_t)p.Ho * p.Wo;
-  float* out = p.heat + ((size_t)b * p.R + row) * hw_out;
+  float* out = p.heat + ((size_t)b * p.R + row) * p.row_f;
   float* P = lds_p + (size_t)wave * p.S;
   // the parked low-res map -> LDS (this wave only); every load has returned
   // before the first store below can overwrite it
@@ -943,7 +960,7 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   const RowGeom g{p.H, p.W, p.S, p.Ho, p.Wo, p.magic_w};
   float bv;
   int bi;
-  expand_row<SMALLW>(P, out, g, lane, p.idx != nullptr, bv, bi);
+  expand_row<SMALLW, BF16>(P, out, g, lane, p.idx != nullptr, bv, bi);
   if (p.idx && lane == 0) write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + row, bv, bi, p.Ho, p.Wo);
 }
 
@@ -997,7 +1014,9 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R);
   if (!sp.ok) return hipErrorInvalidConfiguration;
   const long long crops_pad = (long long)(a.B + kXcds - 1) / kXcds * kXcds;
-  const CombLayout cl = comb_layout(a.C, S);
+  float* const heat = static_cast<float*>(a.heat);
+  const size_t row_f = (size_t)(a.heat_bf16 ? 8 : 16) * S;  // floats per heatmap row
+  const CombLayout cl = comb_layout(a.C, S, (long long)row_f);
 
   if (a.kv != nullptr && a.kt != nullptr) {
     PrepParams np;
@@ -1012,7 +1031,8 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
     np.groups_per_crop = ceil_div(a.R, kPWaves);
     np.comb_hi = cl.hi;
     np.comb_lo = cl.lo;
-    np.heat = a.heat;
+    np.heat = heat;
+    np.row_f = row_f;
     const long long ngrid = (long long)a.B * np.groups_per_crop;
     if (ngrid > INT_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(row_prep_kernel, dim3((unsigned)ngrid), dim3(kPWaves * kWave), 0, stream,
@@ -1042,7 +1062,8 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.comb_hi = (a.kv != nullptr && a.kt != nullptr) ? cl.hi : 0;
   cp.comb_lo = (a.kv != nullptr && a.kt != nullptr) ? cl.lo : 0;
   cp.light_arows = kLightArows;
-  cp.heat = a.heat;
+  cp.heat = heat;
+  cp.row_f = row_f;
   const long long cgrid = crops_pad * cp.items_per_crop;
   if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(contract_kernel, dim3((unsigned)cgrid), dim3(kCThreads), sp.contract_lds,
@@ -1063,18 +1084,24 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   ep.wpg = sp.wpg;
   ep.groups_per_crop = ceil_div(a.R, sp.wpg);
   ep.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
-  ep.heat = a.heat;
+  ep.heat = heat;
+  ep.row_f = row_f;
   ep.idx = a.idx;
   ep.xy = a.xy;
   ep.score = a.score;
   const long long egrid = crops_pad * ep.groups_per_crop;
   if (egrid > INT_MAX) return hipErrorInvalidConfiguration;
-  if (a.W <= kWave)
-    hipLaunchKernelGGL((expand_kernel<true>), dim3((unsigned)egrid), dim3(kEThreads),
-                       sp.expand_lds, stream, ep);
-  else
-    hipLaunchKernelGGL((expand_kernel<false>), dim3((unsigned)egrid), dim3(kEThreads),
-                       sp.expand_lds, stream, ep);
+#define GKD_EXPAND(SW, BF)                                                                   \
+  hipLaunchKernelGGL((expand_kernel<SW, BF>), dim3((unsigned)egrid), dim3(kEThreads),        \
+                     sp.expand_lds, stream, ep)
+  if (a.W <= kWave) {
+    if (a.heat_bf16) GKD_EXPAND(true, true);
+    else GKD_EXPAND(true, false);
+  } else {
+    if (a.heat_bf16) GKD_EXPAND(false, true);
+    else GKD_EXPAND(false, false);
+  }
+#undef GKD_EXPAND
   return hipGetLastError();
 }
 

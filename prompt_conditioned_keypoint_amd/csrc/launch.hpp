@@ -15,7 +15,8 @@ struct HeatmapArgs {
   const uint8_t* mt;
   int B, C, H, W, R;
   bool bf16;
-  float* heat;
+  void* heat;      // [B,R,4H,4W] float32, or bfloat16 when heat_bf16
+  bool heat_bf16;
   int32_t* idx;
   float* xy;
   float* score;

@@ -52,7 +52,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 1
+    assert lib.gkd_abi_version() == 2
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
@@ -80,7 +80,8 @@ def dec(lib, heat=A, valid=None, B=2, R=80, Ho=96, Wo=96, flags=0, idx=A, xy=A2,
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(flags=1), UNSUP),
+    (dict(flags=2), UNSUP),              # only GKD_HEATMAP_BF16 (0x1) is defined
+    (dict(flags=0x80000001), UNSUP),
     (dict(dtype=2), DTYPE),
     (dict(dtype=-1), DTYPE),
     (dict(B=-1), SHAPE),
@@ -109,7 +110,8 @@ def test_kernel_heatmap_rejects(lib, kw, status):
     assert lib.gkd_last_error().decode() != ""
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(R=0), dict(B=0, query=None, heat=None)])
+@pytest.mark.parametrize("kw", [dict(B=0), dict(R=0), dict(B=0, query=None, heat=None),
+                                dict(B=0, flags=1)])
 def test_kernel_heatmap_empty_batch_is_ok(lib, kw):
     assert hm(lib, **kw) == OK
     assert lib.gkd_last_error().decode() == ""
@@ -161,7 +163,7 @@ def test_peak_decode_empty_batch_is_ok(lib):
 
 def test_last_error_is_thread_local(lib):
     import threading
-    assert hm(lib, flags=1) == UNSUP
+    assert hm(lib, flags=2) == UNSUP
     seen = {}
 
     def other():

@@ -291,6 +291,78 @@ def test_ragged_shapes(gkd, ora, dtype, shape):
     check_protos(pv.float().cpu().numpy(), op, mv, dtype, np.abs(q).reshape(B, -1).max(1))
 
 
+BF16_SENTINEL = 0x7FC1  # bfloat16 NaN pattern no rounding produces
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 64, 8, 8, 16), (5, 256, 24, 24, 80), (2, 64, 32, 32, 8),
+                                   (3, 256, 4, 4, 12), (3, 40, 5, 7, 19), (2, 64, 8, 8, 200)])
+def test_bf16_heatmap_output(gkd, ora, dtype, shape):
+    """GKD_HEATMAP_BF16: every valid heatmap value is the same call's float32
+    value rounded to nearest even, bit for bit (streamed path, rows too short
+    to park the combined kernels, several row blocks, and the general kernel
+    for float32 features and odd channel counts); the fused decode is the
+    float32 one; rows with no mask are not written; against the oracle within
+    the bfloat16 row tolerance."""
+    B, C, H, W, R = shape
+    rng = np.random.default_rng(7 * B + C + 11 * H + W + R)
+    q = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    kv = rng.standard_normal((B, R, C)).astype(np.float32)
+    kt = rng.standard_normal((B, R, C)).astype(np.float32)
+    mv = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mt = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mv[0, 0] = mt[0, 0] = 1
+    if B > 1:
+        mv[1] = mt[1] = 0
+    if dtype == "bf16":
+        q, kv, kt = (gkdsynth.round_bf16_f32(a) for a in (q, kv, kt))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"[bf16-heat] {dtype} {shape}", flush=True)
+    args = (dev_tensor(q, dt), dev_tensor(kv, dt), dev_tensor(mv), dev_tensor(kt, dt),
+            dev_tensor(mt))
+    h32, (i32, xy32, s32) = gkd.kernel_heatmap(*args, out=sentinel((B, R, 4 * H, 4 * W)))
+    out16 = torch.full((B, R, 4 * H, 4 * W), BF16_SENTINEL, dtype=torch.int16,
+                       device="cuda").view(torch.bfloat16)
+    h16, (i16, xy16, s16) = gkd.kernel_heatmap(*args, out=out16, heat_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert h16.dtype == torch.bfloat16 and h16.data_ptr() == out16.data_ptr()
+    valid = torch.from_numpy(((mv | mt) > 0)).cuda()
+    bits16 = h16.view(torch.int16)
+    ref16 = h32.to(torch.bfloat16).view(torch.int16)  # torch rounds to nearest even
+    assert torch.equal(bits16[valid], ref16[valid])
+    assert bool((bits16[~valid] == BF16_SENTINEL).all())
+    assert torch.equal(i16, i32)
+    assert torch.equal(xy16.view(torch.int32), xy32.view(torch.int32))
+    assert torch.equal(s16.view(torch.int32), s32.view(torch.int32))
+    oh = ora.kernel_heatmap(q, kv, mv, kt, mt)
+    check_heatmaps(h16.float().cpu().numpy(), oh, valid.cpu().numpy().astype(np.uint8), "bf16",
+                   floors_of(q))
+
+
+def test_bf16_heatmap_output_longtail(gkd):
+    """The long-tail batch with bfloat16 heatmaps: equal to the float32
+    heatmaps of the same call rounded to nearest even on every valid row,
+    same decode."""
+    d = workload("longtail_bf16")
+    q = dev_tensor(d["query"], torch.bfloat16)
+    kv = dev_tensor(np.nan_to_num(gkdsynth.round_bf16_f32(np.random.default_rng(3).standard_normal(
+        (d["B"], d["R"], d["C"])).astype(np.float32))), torch.bfloat16)
+    mv, mt = dev_tensor(d["mask_vis"]), dev_tensor(d["mask_txt"])
+    kt = dev_tensor(np.nan_to_num(d["kern_txt"]), torch.bfloat16)
+    B, R, H, W = d["B"], d["R"], d["H"], d["W"]
+    print("[bf16-heat] longtail", flush=True)
+    h32, dec32 = gkd.kernel_heatmap(q, kv, mv, kt, mt, out=sentinel((B, R, 4 * H, 4 * W)))
+    out16 = torch.full((B, R, 4 * H, 4 * W), BF16_SENTINEL, dtype=torch.int16,
+                       device="cuda").view(torch.bfloat16)
+    h16, dec16 = gkd.kernel_heatmap(q, kv, mv, kt, mt, out=out16, heat_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    valid = (mv > 0) | (mt > 0)
+    assert torch.equal(h16.view(torch.int16)[valid], h32.to(torch.bfloat16).view(torch.int16)[valid])
+    assert bool((h16.view(torch.int16)[~valid] == BF16_SENTINEL).all())
+    for a16, a32 in zip(dec16, dec32):
+        assert torch.equal(a16.view(torch.int32), a32.view(torch.int32))
+
+
 @pytest.mark.parametrize("shape,p_valid", [
     ((3, 48, 9, 8, 30), 0.6),      # H not a multiple of the row-ring depth; C < one block
     ((2, 32, 5, 16, 12), 0.7),     # short maps, no cross-item prefetch
