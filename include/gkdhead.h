@@ -144,9 +144,16 @@ GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
  *                                from its float32 result). The fused decode
  *                                takes the peak and score from the float32
  *                                values in both formats.
+ *                                heatmaps NULL = keypoints only: with the
+ *                                decode outputs set, only they are computed
+ *                                (no heatmap byte is written anywhere; on
+ *                                bf16 features with H*W <= 576 the peak is
+ *                                found in the contraction's epilogue).
  *   peak_idx   [B,R]   int32     optional fused decode (see gkd_peak_decode);
  *   peak_xy    [B,R,2] float32   all three NULL = no decode, else all three
  *   peak_score [B,R]   float32   non-NULL. Rows with no mask get the sentinel.
+ *                                heatmaps and the decode outputs cannot all
+ *                                be NULL (GKD_ERR_NULL).
  * Limits: C >= 1, H >= 1, W >= 1, H*W <= 16384 (else GKD_ERR_UNSUPPORTED).
  */
 GKD_API gkd_status gkd_kernel_heatmap(const void *query, const void *kern_vis,

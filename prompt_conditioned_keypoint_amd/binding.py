@@ -123,14 +123,16 @@ def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
 
 def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=None,
                    mask_txt=None, decode: bool = True, out=None, out_decode=None,
-                   heat_dtype=torch.float32):
+                   heat_dtype=torch.float32, with_heatmaps: bool = True):
     """query [B,C,H,W] (f32|bf16); kern_* [B,R,C] in the query dtype with
     mask_* [B,R] u8 (None = modality absent).
 
     Returns heatmaps [B,R,4H,4W] in heat_dtype (float32, or bfloat16 via
     the GKD_HEATMAP_BF16 flag) and, if decode, (idx [B,R] i32, xy [B,R,2]
     f32, score [B,R] f32). Rows with no mask set are not written (they keep
-    whatever `out` held)."""
+    whatever `out` held). with_heatmaps=False computes the keypoints only
+    (heatmaps NULL in the C call; decode must be True) and returns
+    (idx, xy, score)."""
     lib = load()
     _dev(query, "query", ndim=4)
     B, C, H, W = query.shape
@@ -150,11 +152,17 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
     if heat_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"heat_dtype must be float32 or bfloat16, got {heat_dtype}")
     flags = GKD_HEATMAP_BF16 if heat_dtype == torch.bfloat16 else 0
-    if out is None:
+    if not with_heatmaps:
+        if not decode:
+            raise ValueError("with_heatmaps=False needs decode=True")
+        if out is not None:
+            raise ValueError("with_heatmaps=False takes no heatmap buffer")
+    elif out is None:
         out = torch.empty((B, R, 4 * H, 4 * W), dtype=heat_dtype, device=query.device)
-    _dev(out, "out", heat_dtype)
-    if out.shape != (B, R, 4 * H, 4 * W):
-        raise ValueError("out must be [B,R,4H,4W]")
+    if out is not None:
+        _dev(out, "out", heat_dtype)
+        if out.shape != (B, R, 4 * H, 4 * W):
+            raise ValueError("out must be [B,R,4H,4W]")
     idx = xy = score = None
     if decode:
         if out_decode is None:
@@ -167,6 +175,8 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
                                   _ptr(kern_txt), _ptr(mask_txt), B, C, H, W, R,
                                   _dtype_code(query), flags, _ptr(out), _ptr(idx), _ptr(xy),
                                   _ptr(score), _stream(query.device)))
+    if not with_heatmaps:
+        return idx, xy, score
     if decode:
         return out, (idx, xy, score)
     return out

@@ -116,15 +116,16 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
                 (long long)H * W, gkd::kHeatmapMaxS);
   {
     const bool bf16 = dtype == GKD_DTYPE_BF16;
-    const bool fits = gkd::heatmap_stream_applicable(C, H * W, bf16)
-                          ? gkd::plan_heatmap_stream(B, C, H * W, R).ok
+    const bool kp = heatmaps == nullptr;
+    const bool fits = gkd::heatmap_stream_applicable(C, H * W, bf16, kp)
+                          ? gkd::plan_heatmap_stream(B, C, H * W, R, kp).ok
                           : gkd::plan_heatmap(C, H * W, bf16).rows_per_item >= 1;
     if (!fits)
       return fail(GKD_ERR_UNSUPPORTED,
                   "gkd_kernel_heatmap: H*W=%d does not fit the kernel's LDS budget", H * W);
   }
   if (B == 0 || R == 0) return ok();
-  if (!query || !heatmaps) return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: NULL query/heatmaps");
+  if (!query) return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: NULL query");
   if ((kern_vis == nullptr) != (mask_vis == nullptr) ||
       (kern_txt == nullptr) != (mask_txt == nullptr))
     return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: a kernel/mask pair is half NULL");
@@ -133,7 +134,10 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   const int ndec = (peak_idx != nullptr) + (peak_xy != nullptr) + (peak_score != nullptr);
   if (ndec != 0 && ndec != 3)
     return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: decode outputs must be all NULL or all set");
-  if (!aligned16(query) || !aligned16(heatmaps) || (kern_vis && !aligned16(kern_vis)) ||
+  if (!heatmaps && ndec == 0)
+    return fail(GKD_ERR_NULL, "gkd_kernel_heatmap: NULL heatmaps and no decode outputs");
+  if (!aligned16(query) || (heatmaps && !aligned16(heatmaps)) ||
+      (kern_vis && !aligned16(kern_vis)) ||
       (kern_txt && !aligned16(kern_txt)))
     return fail(GKD_ERR_ALIGN, "gkd_kernel_heatmap: query/kernels/heatmaps need 16-byte alignment");
   if (ndec && (!aligned4(peak_idx) || !aligned4(peak_xy) || !aligned4(peak_score)))

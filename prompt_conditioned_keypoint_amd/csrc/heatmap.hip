@@ -391,7 +391,9 @@ void heatmap_kernel(HmParams p) {
         for (int e = 0; e < 4; ++e) o[e] = fmaf(yh[d], hi[e], yl[d] * lo[e]);
         const int y = 4 * i + d;
         const size_t e = out_e + (size_t)y * Wo + 4 * j;
-        if (p.heat_bf16) {
+        if (p.heat == nullptr) {
+          // keypoints only: nothing is stored
+        } else if (p.heat_bf16) {
           // round to nearest even; the peak below still uses the float32 values
           const u32x2 v = {
               __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[0], o[1]}, bf16x2)),
@@ -464,7 +466,8 @@ HeatmapPlan plan_heatmap(int C, int S, bool bf16) {
 }
 
 hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream) {
-  if (heatmap_stream_applicable(a.C, a.H * a.W, a.bf16)) return launch_heatmap_stream(a, stream);
+  if (heatmap_stream_applicable(a.C, a.H * a.W, a.bf16, a.heat == nullptr))
+    return launch_heatmap_stream(a, stream);
   HmParams p;
   p.query = a.query;
   p.kv = a.kv;

@@ -105,9 +105,12 @@ struct RowGeom {
 // rows, so every output of a later cell has a larger flat index than any
 // output of an earlier one; the lane keeps (best value, its cell) with a
 // strict > and finds the position inside the cell once, at the end.
-// BF16: the row is stored as bfloat16 (each value rounded to nearest even
-// from the float32 result; the peak is still taken on the float32 values).
-template <bool SMALLW, bool BF16>
+// OUT: kOutF32 stores float32; kOutBf16 stores bfloat16 (each value
+// rounded to nearest even from the float32 result; the peak is still taken
+// on the float32 values); kOutNone stores nothing and only finds the peak,
+// with the same arithmetic.
+constexpr int kOutNone = 0, kOutF32 = 1, kOutBf16 = 2;
+template <bool SMALLW, int OUT>
 __device__ __forceinline__ void expand_row(const float* P, void* out_row, const RowGeom& g,
                                            int lane, bool decode, float& best_v, int& best_i) {
   float bv = -INFINITY;
@@ -117,7 +120,7 @@ __device__ __forceinline__ void expand_row(const float* P, void* out_row, const 
     float o[16];
     cell_values(P, i, j, g.H, g.W, o);
     const size_t e0 = (size_t)(4 * i) * g.Wo + 4 * j;  // element of output (4i, 4j)
-    if constexpr (BF16) {
+    if constexpr (OUT == kOutBf16) {
       uint16_t* dst = static_cast<uint16_t*>(out_row) + e0;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -126,7 +129,7 @@ __device__ __forceinline__ void expand_row(const float* P, void* out_row, const 
             __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[4 * d + 2], o[4 * d + 3]}, bf16x2))};
         __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(dst + (size_t)d * g.Wo));
       }
-    } else {
+    } else if constexpr (OUT == kOutF32) {
       float* dst = static_cast<float*>(out_row) + e0;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -225,8 +228,16 @@ struct ContractParams {
   int nchunks, rblocks, items_per_crop, nsteps;
   int comb_hi, comb_lo;  // CombLayout of the rows of two-modality crops (0: none)
   int light_arows;       // items staging at most this many kernel rows load one step ahead
-  float* heat;           // heatmap rows, viewed as floats (parking space)
+  float* heat;           // heatmap rows, viewed as floats (parking space); null: keypoints only
   size_t row_f;          // floats per heatmap row: 16 H*W (float32) or 8 H*W (bfloat16)
+  const float* wsrc;     // fusion weights (w_v, w_t) of row r at wsrc + r * w_stride, for the
+  size_t w_stride;       //   step-by-step combination
+  // keypoints only (heat null): the decode runs in the epilogue; every
+  // item then covers whole maps (one pixel chunk)
+  int32_t* idx;
+  float* xy;
+  float* score;
+  uint64_t magic_w;      // ceil(2^32 / W)
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 layout:
@@ -533,6 +544,47 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   }
   lds_barrier();  // the ring is free; the weights are visible
 
+  if (p.heat == nullptr) {
+    // keypoints only: the fused low-res maps go to the (now free) ring in
+    // passes of whole rows, and each wave finds the peak of the 4x
+    // expansion of its rows with the expand pass's arithmetic, storing
+    // nothing but the keypoint
+    float* Pl = reinterpret_cast<float*>(lds);
+    const int rows_per_pass = (int)(kContractLds / ((size_t)p.S * 4));
+    const RowGeom g{p.H, p.W, p.S, 4 * p.H, 4 * p.W, p.magic_w};
+    for (int base = 0; base < it.nsel; base += rows_per_pass) {
+#pragma unroll
+      for (int u = 0; u < UPW; ++u) {
+        const int h = h0 + u * hstep;
+        if (h >= it.MH) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 16 * h + 4 * g4 + i;
+          if (slot < base || slot >= base + rows_per_pass || slot >= it.nsel) continue;
+          const float w = TWO ? 1.f : s_w[0][slot];
+          float* dst = Pl + (size_t)(slot - base) * p.S + gpx + n16;
+#pragma unroll
+          for (int t = 0; t < 3; ++t)
+            if (gpx + 16 * t + n16 < p.S) dst[16 * t] = TWO ? acc[u][t][i] : w * acc[u][t][i];
+        }
+      }
+      lds_barrier();
+      const int nrows = min(rows_per_pass, it.nsel - base);
+      for (int r = wave; r < nrows; r += kCWaves) {
+        float bv;
+        int bi;
+        if (p.W <= kWave)
+          expand_row<true, kOutNone>(Pl + (size_t)r * p.S, nullptr, g, lane, true, bv, bi);
+        else
+          expand_row<false, kOutNone>(Pl + (size_t)r * p.S, nullptr, g, lane, true, bv, bi);
+        if (lane == 0)
+          write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + s_rows[base + r], bv, bi, g.Ho,
+                         g.Wo);
+      }
+      lds_barrier();
+    }
+    return;
+  }
   // fused low-res maps -> the first H*W floats of each row's heatmap,
   // straight from the accumulators: lane (n16, g4) holds rows 4 g4 + i of
   // each M tile at pixel 16 t + n16, so 16 lanes store 64 contiguous bytes
@@ -649,6 +701,19 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
 
   if (wave == 0)
     select_rows(mv, mt, p.R, lane, rblk, kItemRows, s_rows, s_mv, s_mt, &s_nvalid, &s_nsel);
+  // keypoints only: the crop's first item writes the sentinels of its rows
+  // with no mask set (the weights parked in peak_xy belong to valid rows)
+  if (p.heat == nullptr && rblk == 0 && wave == kCWaves - 1) {
+    for (int r = lane; r < p.R; r += kWave) {
+      if (!((mv && mv[r]) || (mt && mt[r]))) {
+        const size_t o = (size_t)b * p.R + r;
+        p.idx[o] = -1;
+        p.xy[2 * o] = __builtin_nanf("");
+        p.xy[2 * o + 1] = __builtin_nanf("");
+        p.score[o] = -INFINITY;
+      }
+    }
+  }
   __syncthreads();
   it.nsel = s_nsel;
   if (it.nsel == 0) {
@@ -682,7 +747,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
     const int wm = e / kItemRows, wslot = e - wm * kItemRows;
     if (e < 2 * kItemRows && wslot < it.nsel)
       __builtin_amdgcn_global_load_lds(
-          (glb_void*)(p.heat + ((size_t)b * p.R + s_rows[wslot]) * p.row_f + p.S + wm),
+          (glb_void*)(p.wsrc + ((size_t)b * p.R + s_rows[wslot]) * p.w_stride + wm),
           (lds_void*)(&s_w[0][0] + wave * kWave), 4, 0, 0);
   }
   const int nA = it.arows * kRowSlots;          // kernel-row slots of a step pair
@@ -780,6 +845,8 @@ struct PrepParams {
   int comb_hi, comb_lo; // CombLayout (0: park the weights)
   float* heat;
   size_t row_f;         // floats per heatmap row
+  float* wout;          // parked fusion weights of row r: wout + r * w_stride (+0 v, +1 t)
+  size_t w_stride;
 };
 
 __device__ __forceinline__ float sum_squares8(u32x4 x) {
@@ -852,14 +919,15 @@ __global__ __launch_bounds__(kPWaves * kWave) void row_prep_kernel(PrepParams p)
   const float n = (float)((int)v + (int)t);
   const float wv = v ? 1.f / (fmaxf(sqrtf(ssv), 1e-12f) * n) : 0.f;
   const float wt = t ? 1.f / (fmaxf(sqrtf(sst), 1e-12f) * n) : 0.f;
-  float* h = p.heat + ((size_t)b * p.R + r) * p.row_f;
   if (p.comb_hi == 0) {
     if (lane == 0) {
-      h[p.S] = wv;
-      h[p.S + 1] = wt;
+      float* wd = p.wout + ((size_t)b * p.R + r) * p.w_stride;
+      wd[0] = wv;
+      wd[1] = wt;
     }
     return;
   }
+  float* h = p.heat + ((size_t)b * p.R + r) * p.row_f;
   // the combination, 8 channels per lane and block; an absent modality
   // enters as zeros
   uint16_t* const hr = reinterpret_cast<uint16_t*>(h + p.comb_hi);
@@ -960,7 +1028,7 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   const RowGeom g{p.H, p.W, p.S, p.Ho, p.Wo, p.magic_w};
   float bv;
   int bi;
-  expand_row<SMALLW, BF16>(P, out, g, lane, p.idx != nullptr, bv, bi);
+  expand_row<SMALLW, BF16 ? kOutBf16 : kOutF32>(P, out, g, lane, p.idx != nullptr, bv, bi);
   if (p.idx && lane == 0) write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + row, bv, bi, p.Ho, p.Wo);
 }
 
@@ -968,19 +1036,22 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
-bool heatmap_stream_applicable(int C, int S, bool bf16) {
-  return bf16 && C % kKS == 0 && S % 16 == 0 && S <= kHeatmapMaxS;
+bool heatmap_stream_applicable(int C, int S, bool bf16, bool keypoints_only) {
+  // keypoints only: one workgroup's 12 wave groups must cover the whole map
+  return bf16 && C % kKS == 0 && S % 16 == 0 && S <= kHeatmapMaxS &&
+         (!keypoints_only || S <= kCWaves * kGroupPx);
 }
 
-StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
+StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps) {
   StreamPlan sp;
   // wave groups per chunk: the fewest that still cover a small map in one
-  // chunk, then fewer still while the batch leaves CUs idle
+  // chunk, then fewer still while the batch leaves CUs idle (not when every
+  // item must cover whole maps)
   static const int kNgSteps[] = {12, 6, 4, 3, 2, 1};
   int k = 0;
   while (k + 1 < 6 && kNgSteps[k + 1] * kGroupPx >= S) ++k;
   const int rblocks = ceil_div(R, kItemRows);
-  while (k + 1 < 6 &&
+  while (!whole_maps && k + 1 < 6 &&
          (long long)B * ceil_div(S, kNgSteps[k] * kGroupPx) * rblocks < 240)
     ++k;
   sp.ng = kNgSteps[k];
@@ -1005,18 +1076,24 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R) {
   sp.wpg = S <= 4096 ? kEWaves : 1;
   sp.expand_lds = (size_t)sp.wpg * S * sizeof(float);
   sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kContractLds &&
-          sp.expand_lds <= 64 * 1024;
+          sp.expand_lds <= 64 * 1024 && (!whole_maps || sp.nchunks == 1);
   return sp;
 }
 
 hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   const int S = a.H * a.W;
-  const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R);
+  const bool kp = a.heat == nullptr;  // keypoints only
+  const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R, kp);
   if (!sp.ok) return hipErrorInvalidConfiguration;
   const long long crops_pad = (long long)(a.B + kXcds - 1) / kXcds * kXcds;
   float* const heat = static_cast<float*>(a.heat);
-  const size_t row_f = (size_t)(a.heat_bf16 ? 8 : 16) * S;  // floats per heatmap row
-  const CombLayout cl = comb_layout(a.C, S, (long long)row_f);
+  const size_t row_f = kp ? 0 : (size_t)(a.heat_bf16 ? 8 : 16) * S;  // floats per heatmap row
+  // no heatmap rows: the two-prompt rows combine step by step, with their
+  // fusion weights parked in peak_xy (two floats per row, overwritten by
+  // the decode)
+  const CombLayout cl = kp ? CombLayout{} : comb_layout(a.C, S, (long long)row_f);
+  float* const wpark = kp ? a.xy : heat + S;
+  const size_t wstride = kp ? 2 : row_f;
 
   if (a.kv != nullptr && a.kt != nullptr) {
     PrepParams np;
@@ -1033,6 +1110,8 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
     np.comb_lo = cl.lo;
     np.heat = heat;
     np.row_f = row_f;
+    np.wout = wpark;
+    np.w_stride = wstride;
     const long long ngrid = (long long)a.B * np.groups_per_crop;
     if (ngrid > INT_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(row_prep_kernel, dim3((unsigned)ngrid), dim3(kPWaves * kWave), 0, stream,
@@ -1064,12 +1143,18 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.light_arows = kLightArows;
   cp.heat = heat;
   cp.row_f = row_f;
+  cp.wsrc = wpark;
+  cp.w_stride = wstride;
+  cp.idx = a.idx;
+  cp.xy = a.xy;
+  cp.score = a.score;
+  cp.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
   const long long cgrid = crops_pad * cp.items_per_crop;
   if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(contract_kernel, dim3((unsigned)cgrid), dim3(kCThreads), sp.contract_lds,
                      stream, cp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || kp) return e;
 
   ExpandParams ep;
   ep.mv = a.mv;

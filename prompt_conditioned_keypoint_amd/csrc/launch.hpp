@@ -15,7 +15,7 @@ struct HeatmapArgs {
   const uint8_t* mt;
   int B, C, H, W, R;
   bool bf16;
-  void* heat;      // [B,R,4H,4W] float32, or bfloat16 when heat_bf16
+  void* heat;      // [B,R,4H,4W] float32, or bfloat16 when heat_bf16; null: keypoints only
   bool heat_bf16;
   int32_t* idx;
   float* xy;
@@ -62,8 +62,10 @@ struct StreamPlan {
   size_t contract_lds = 0, expand_lds = 0;
   bool ok = false;
 };
-bool heatmap_stream_applicable(int C, int S, bool bf16);
-StreamPlan plan_heatmap_stream(int B, int C, int S, int R);
+// keypoints_only / whole_maps: no heatmaps are written and the decode runs
+// in the contraction, so every item must cover whole maps
+bool heatmap_stream_applicable(int C, int S, bool bf16, bool keypoints_only);
+StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps);
 hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream);
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -94,7 +94,9 @@ def dec(lib, heat=A, valid=None, B=2, R=80, Ho=96, Wo=96, flags=0, idx=A, xy=A2,
     (dict(H=129, W=128, R=1), UNSUP),          # H*W beyond the kernel's limit
     (dict(H=1, W=16385, R=1, dtype=0), UNSUP),
     (dict(query=None), NULL),
-    (dict(heat=None), NULL),
+    (dict(heat=None), NULL),                   # neither heatmaps nor keypoints
+    (dict(heat=None, idx=A), NULL),            # keypoints only, decode outputs half set
+    (dict(heat=None, idx=A, xy=A2 + 1, score=A3), ALIGN),  # keypoints only reaches the checks
     (dict(mv=None), NULL),                     # half a kernel/mask pair
     (dict(kt=A2), NULL),
     (dict(kv=None, mv=None), NULL),            # no modality at all

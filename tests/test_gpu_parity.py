@@ -291,6 +291,70 @@ def test_ragged_shapes(gkd, ora, dtype, shape):
     check_protos(pv.float().cpu().numpy(), op, mv, dtype, np.abs(q).reshape(B, -1).max(1))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 64, 8, 8, 16), (5, 256, 24, 24, 80), (2, 64, 8, 8, 200),
+                                   (1, 32, 2, 72, 6), (3, 256, 4, 4, 12), (3, 40, 5, 7, 19),
+                                   (2, 64, 32, 32, 8), (9, 128, 24, 24, 37)])
+def test_keypoints_only(gkd, ora, dtype, shape):
+    """Heatmaps NULL: the keypoints equal, bit for bit, those of the same
+    call with heatmaps (the contraction finds the peaks itself on bf16
+    features with H*W <= 576: several row blocks, W > 64, one and both
+    prompts; otherwise the general kernel runs without stores), rows with no
+    mask get the sentinel, and they agree with the oracle's decode (maps of
+    bf16 features beyond 576 pixels decode in the general kernel, so there
+    only the oracle comparison applies)."""
+    B, C, H, W, R = shape
+    rng = np.random.default_rng(5 * B + C + 13 * H + W + R)
+    q = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    kv = rng.standard_normal((B, R, C)).astype(np.float32)
+    kt = rng.standard_normal((B, R, C)).astype(np.float32)
+    mv = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mt = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mv[0, 0] = mt[0, 0] = 1
+    if B > 1:
+        mv[1] = mt[1] = 0
+    if B > 2:
+        mt[2] = 0                    # a crop with one prompt only
+    if dtype == "bf16":
+        q, kv, kt = (gkdsynth.round_bf16_f32(a) for a in (q, kv, kt))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"[kp-only] {dtype} {shape}", flush=True)
+    args = (dev_tensor(q, dt), dev_tensor(kv, dt), dev_tensor(mv), dev_tensor(kt, dt),
+            dev_tensor(mt))
+    heat, full = gkd.kernel_heatmap(*args, out=sentinel((B, R, 4 * H, 4 * W)))
+    fill = lambda shp, dtp: sentinel(shp, dtp) if dtp == torch.int32 else sentinel(shp)
+    kp = (fill((B, R), torch.int32), fill((B, R, 2), torch.float32), fill((B, R), torch.float32))
+    got = gkd.kernel_heatmap(*args, out_decode=kp, with_heatmaps=False)
+    torch.cuda.synchronize()
+    # bf16 maps larger than one workgroup's pixel chunk (576) take the
+    # streamed path with heatmaps but the general kernel without: another
+    # summation order, so only the oracle comparison below applies there
+    same_path = not (dtype == "bf16" and C % 32 == 0 and (H * W) % 16 == 0 and H * W > 576)
+    if same_path:
+        for g, f in zip(got, full):
+            assert torch.equal(g.view(torch.int32), f.view(torch.int32))
+    oh = ora.kernel_heatmap(q, kv, mv, kt, mt)
+    valid = ((mv | mt) > 0).astype(np.uint8)
+    check_decode(tuple(t.cpu().numpy() for t in got), oh, valid, dtype, floors=floors_of(q))
+
+
+def test_keypoints_only_longtail(gkd):
+    """The long-tail batch, keypoints only: equal to the decode of the call
+    with heatmaps, bit for bit."""
+    d = workload("longtail_bf16")
+    q = dev_tensor(d["query"], torch.bfloat16)
+    kv = dev_tensor(np.nan_to_num(gkdsynth.round_bf16_f32(np.random.default_rng(3).standard_normal(
+        (d["B"], d["R"], d["C"])).astype(np.float32))), torch.bfloat16)
+    mv, mt = dev_tensor(d["mask_vis"]), dev_tensor(d["mask_txt"])
+    kt = dev_tensor(np.nan_to_num(d["kern_txt"]), torch.bfloat16)
+    print("[kp-only] longtail", flush=True)
+    _, full = gkd.kernel_heatmap(q, kv, mv, kt, mt)
+    got = gkd.kernel_heatmap(q, kv, mv, kt, mt, with_heatmaps=False)
+    torch.cuda.synchronize()
+    for g, f in zip(got, full):
+        assert torch.equal(g.view(torch.int32), f.view(torch.int32))
+
+
 BF16_SENTINEL = 0x7FC1  # bfloat16 NaN pattern no rounding produces
 
 
