@@ -243,10 +243,11 @@ def main():
 
     heat16 = None  # bfloat16 heatmaps (GKD_HEATMAP_BF16), for the secondary mode
 
-    def step(ev=None, ev_vkp=None, bf16_heat=False):
+    def step(ev=None, ev_vkp=None, bf16_heat=False, kp_only=False):
         # ev: events around the heatmap call (the roofline's kernel);
         # ev_vkp: around the VKP launch (a separate, untimed pass);
-        # bf16_heat: the same step with bfloat16 heatmaps (a separate pass)
+        # bf16_heat / kp_only: the same step with bfloat16 heatmaps, or with
+        # the keypoints only (separate passes)
         if ev_vkp is not None:
             ev_vkp[0].record()
         if has_vis:
@@ -255,10 +256,15 @@ def main():
             ev_vkp[1].record()
         if ev is not None:
             ev[0].record()
-        gkd.kernel_heatmap(q, protos if has_vis else None, mv if has_vis else None,
-                           kt if has_txt else None, mt if has_txt else None,
-                           out=heat16 if bf16_heat else heat, out_decode=(idx, xy, score),
-                           heat_dtype=torch.bfloat16 if bf16_heat else torch.float32)
+        if kp_only:
+            gkd.kernel_heatmap(q, protos if has_vis else None, mv if has_vis else None,
+                               kt if has_txt else None, mt if has_txt else None,
+                               out_decode=(idx, xy, score), with_heatmaps=False)
+        else:
+            gkd.kernel_heatmap(q, protos if has_vis else None, mv if has_vis else None,
+                               kt if has_txt else None, mt if has_txt else None,
+                               out=heat16 if bf16_heat else heat, out_decode=(idx, xy, score),
+                               heat_dtype=torch.bfloat16 if bf16_heat else torch.float32)
         if ev is not None:
             ev[1].record()
 
@@ -304,6 +310,19 @@ def main():
     heat16_bytes = heat_bytes - rows * 16 * H * W * 2  # 2 of the 4 bytes per heatmap value
     del heat16
     heat16 = None
+
+    # and with the keypoints only (no heatmaps at all)
+    for _ in range(args.warmup):
+        step(kp_only=True)
+    evk = [[TimingEvent(torch) for _ in range(2)] for _ in range(n16)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(n16):
+        step(evk[k], kp_only=True)
+    torch.cuda.synchronize()
+    mskp = (time.perf_counter() - t0) * 1e3 / n16
+    hmkp = float(np.mean([e[0].elapsed_time(e[1]) for e in evk]))
+    kp_bytes = heat_bytes - rows * 16 * H * W * 4  # no heatmap bytes
 
     achieved = heat_bytes / (hm_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
@@ -367,6 +386,13 @@ def main():
                 "heatmaps_per_s": round(rows / (ms16 * 1e-3), 1),
                 "heatmap_call_ms": round(hm16, 4), "heatmap_call_alg_bytes": heat16_bytes,
                 "heatmap_call_gbps": round(heat16_bytes / (hm16 * 1e-3) / 1e9, 1),
+            },
+            "keypoints_only": {
+                "note": "same workload, keypoints only (heatmaps NULL); not the headline",
+                "steps": n16, "ms_per_step": round(mskp, 4),
+                "keypoints_per_s": round(rows / (mskp * 1e-3), 1),
+                "call_ms": round(hmkp, 4), "call_alg_bytes": kp_bytes,
+                "call_gbps": round(kp_bytes / (hmkp * 1e-3) / 1e9, 1),
             },
         },
         "parity": parity,
