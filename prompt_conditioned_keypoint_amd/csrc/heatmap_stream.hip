@@ -165,6 +165,106 @@ __device__ __forceinline__ void expand_row(const float* P, void* out_row, const 
   best_i = bi;
 }
 
+// Wave64 maximum (every lane gets it): the argmax lane pattern on values
+// alone.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The first-occurrence peak of the 4x expansion of P (one wave; the same
+// result, bit for bit, as expand_row's scan) without evaluating every cell.
+// Each expanded value is a convex combination of at most four low-res
+// values of its cell's 3x3 neighbourhood, computed in two fma stages whose
+// rounding adds at most about 4 ulp of M = max |P|. With L the peak of the
+// cell holding the maximum of P (a value of the expansion, so a lower bound
+// of its peak) and T = L - M * 2^-20, every output >= L, the peak and all
+// its ties included, lies in the 3x3 neighbourhood of a "hot" cell, one
+// with P >= T. The hot cells are listed in hl (kMaxHot ints of this wave's
+// LDS) and only their neighbourhoods are evaluated, seven hot cells at a
+// time (lane = 9 * slot + neighbour). No hot cell (a NaN in the bound),
+// more than kMaxHot (flat maps) or maps beyond kPeakChunks * 64 cells fall
+// back to the full scan. A lane holds its cells of P in registers.
+constexpr int kMaxHot = 64, kPeakChunks = 9;
+template <bool SMALLW>
+__device__ __forceinline__ void row_peak(const float* P, int* hl, const RowGeom& g, int lane,
+                                         float& best_v, int& best_i) {
+  constexpr int kPerPass = kWave / 9;
+  if (g.S > kPeakChunks * kWave) {
+    expand_row<SMALLW, kOutNone>(P, nullptr, g, lane, true, best_v, best_i);
+    return;
+  }
+  float v[kPeakChunks];
+#pragma unroll
+  for (int k = 0; k < kPeakChunks; ++k) v[k] = k * kWave + lane < g.S ? P[k * kWave + lane] : 0.f;
+  float pv = -INFINITY, amax = 0.f;
+  int pc = INT_MAX;
+#pragma unroll
+  for (int k = 0; k < kPeakChunks; ++k) {
+    const bool in = k * kWave + lane < g.S;
+    amax = in ? fmaxf(amax, fabsf(v[k])) : amax;
+    if (in && v[k] > pv) {  // a lane's cells ascend: strict > keeps the first
+      pv = v[k];
+      pc = k * kWave + lane;
+    }
+  }
+  wave_argmax(pv, pc);
+  amax = wave_max(amax);
+  float o[16];
+  float T = __int_as_float(0x7fc00000);  // NaN: no cell is hot
+  if (pc != INT_MAX) {
+    const int i = (int)(((uint64_t)(uint32_t)pc * g.magic_w) >> 32), j = pc - i * g.W;
+    cell_values(P, i, j, g.H, g.W, o);
+    T = max16(o) - amax * 0x1p-20f;
+  }
+  int nhot = 0;
+#pragma unroll
+  for (int k = 0; k < kPeakChunks; ++k) {
+    const bool h = k * kWave + lane < g.S && v[k] >= T;
+    const uint64_t m = __ballot(h);
+    const int rank = nhot + (int)__builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (h && rank < kMaxHot) hl[rank] = k * kWave + lane;
+    nhot += __popcll(m);
+  }
+  if (nhot == 0 || nhot > kMaxHot) {
+    expand_row<SMALLW, kOutNone>(P, nullptr, g, lane, true, best_v, best_i);
+    return;
+  }
+  __builtin_amdgcn_wave_barrier();  // the list is the wave's own: in-order LDS
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  const int slot = lane / 9, nb = lane - 9 * slot;
+  const int di = nb / 3 - 1, dj = nb % 3 - 1;
+  for (int k0 = 0; k0 < nhot; k0 += kPerPass) {
+    if (slot < kPerPass && k0 + slot < nhot) {
+      const int h = hl[k0 + slot];
+      const int hi = (int)(((uint64_t)(uint32_t)h * g.magic_w) >> 32), hj = h - hi * g.W;
+      int ni = hi + di, nj = hj + dj;  // clamped: a repeated cell repeats a candidate
+      ni = ni < 0 ? 0 : (ni > g.H - 1 ? g.H - 1 : ni);
+      nj = nj < 0 ? 0 : (nj > g.W - 1 ? g.W - 1 : nj);
+      cell_values(P, ni, nj, g.H, g.W, o);
+      const float m = max16(o);
+      const int q = first_of(o, m);
+      const int flat = (4 * ni + (q >> 2)) * g.Wo + 4 * nj + (q & 3);
+      if (better(m, flat, bv, bi)) {
+        bv = m;
+        bi = flat;
+      }
+    }
+  }
+  wave_argmax(bv, bi);
+  best_v = bv;
+  best_i = bi;
+}
+
 // keypoint record of one row: flat index, cell-centre -1..1 coordinates,
 // raw score
 __device__ __forceinline__ void write_keypoint(int32_t* idx, float* xy, float* score, size_t o,
@@ -385,8 +485,8 @@ struct ItemShape {
 
 // K loop, row norms and epilogue for one item. MODE: kVis / kTxt (one
 // modality: the row norms are summed along the K loop and the fusion weight
-// is applied to the finished sums), kComb (both modalities: each step's
-// kernel-row slice is first replaced in LDS by the weighted combination
+// is applied to the finished sums), kComb (both modalities: each pair of
+// steps' kernel-row slices is first replaced in LDS by the weighted combination
 // w_v k_v + w_t k_t, as a bfloat16 hi part over the visual rows and a lo
 // part over the text rows, so a row needs one accumulator and two MFMAs) or
 // kPre (the same hi and lo parts, formed once by the row pass and staged
@@ -426,9 +526,9 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   // column c of staged kernel row a, step by step
   const bool norm_thread = !TWO && tid < 4 * it.arows;
   const int nrow = tid >> 2, ncol = tid & 3;
-  // combination (kComb): thread 8 a + c rewrites bf16 columns 4 c .. 4 c + 3
-  // of row slot a; its weights are read once step 0 (and the weights' DMA
-  // before it) landed
+  // combination (kComb): thread 8 a + c rewrites 16-byte column c (both
+  // steps of a pair) of row slot a; its weights are read once step 0 (and
+  // the weights' DMA before it) landed
   const bool comb_thread = COMB && tid < 8 * arow0;
   const int crow = tid >> 3, ccol = tid & 7;
   float wv = 0.f, wt = 0.f;
@@ -466,24 +566,29 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     const int cur = k % kStages;
     const unsigned char* sb = lds + (size_t)cur * it.fbytes;
     // this step's half (16-byte slots 4 (k & 1) .. + 3) of its pair's rows
-    unsigned char* const sa = aring + (size_t)((k >> 1) % kPairSlots) * it.abytes + 64 * (k & 1);
+    unsigned char* const sp = aring + (size_t)((k >> 1) % kPairSlots) * it.abytes;
+    unsigned char* const sa = sp + 64 * (k & 1);
     if constexpr (COMB) {
-      if (comb_thread) {
-        u32x2* pv = reinterpret_cast<u32x2*>(sa + crow * (kRowSlots * 16) + 8 * ccol);
-        u32x2* pt = reinterpret_cast<u32x2*>(sa + (arow0 + crow) * (kRowSlots * 16) + 8 * ccol);
-        const u32x2 v = *pv, t = *pt;
-        u32x2 hi, lo;
+      // an even step combines the whole pair (its own half and the next
+      // step's), so only every other step waits on a second barrier
+      if ((k & 1) == 0) {
+        if (comb_thread) {
+          u32x4* pv = reinterpret_cast<u32x4*>(sp + crow * (kRowSlots * 16) + 16 * ccol);
+          u32x4* pt = reinterpret_cast<u32x4*>(sp + (arow0 + crow) * (kRowSlots * 16) + 16 * ccol);
+          const u32x4 v = *pv, t = *pt;
+          u32x4 hi, lo;
 #pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          uint32_t h, l;
-          combine_pair(v[d], t[d], wv, wt, h, l);
-          hi[d] = h;
-          lo[d] = l;
+          for (int d = 0; d < 4; ++d) {
+            uint32_t h, l;
+            combine_pair(v[d], t[d], wv, wt, h, l);
+            hi[d] = h;
+            lo[d] = l;
+          }
+          *pv = hi;
+          *pt = lo;
         }
-        *pv = hi;
-        *pt = lo;
+        lds_barrier();  // the combined rows are in place
       }
-      lds_barrier();  // the combined rows are in place
     }
     // B: lane (n16, g4) of N tile t receives channels 8 g4 .. 8 g4 + 7 of
     // pixel gpx + 16 t + n16 from two transposing 8-byte reads (rows
@@ -547,10 +652,17 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   if (p.heat == nullptr) {
     // keypoints only: the fused low-res maps go to the (now free) ring in
     // passes of whole rows, and each wave finds the peak of the 4x
-    // expansion of its rows with the expand pass's arithmetic, storing
-    // nothing but the keypoint
+    // expansion of its rows with the expand pass's arithmetic (row_peak:
+    // only the neighbourhoods that can hold it), storing nothing but the
+    // keypoint
+    // (the ring's last kCWaves * kMaxHot ints hold the waves' hot-cell lists)
     float* Pl = reinterpret_cast<float*>(lds);
-    const int rows_per_pass = (int)(kContractLds / ((size_t)p.S * 4));
+    constexpr size_t kHotBytes = (size_t)kCWaves * kMaxHot * sizeof(int);
+    int* hl = reinterpret_cast<int*>(lds + kContractLds - kHotBytes) + wave * kMaxHot;
+    // rows at a pitch of S + 4 floats: the four row groups of a store land
+    // in different banks
+    const size_t pitch = (size_t)p.S + 4;
+    const int rows_per_pass = (int)((kContractLds - kHotBytes) / (pitch * 4));
     const RowGeom g{p.H, p.W, p.S, 4 * p.H, 4 * p.W, p.magic_w};
     for (int base = 0; base < it.nsel; base += rows_per_pass) {
 #pragma unroll
@@ -562,7 +674,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
           const int slot = 16 * h + 4 * g4 + i;
           if (slot < base || slot >= base + rows_per_pass || slot >= it.nsel) continue;
           const float w = TWO ? 1.f : s_w[0][slot];
-          float* dst = Pl + (size_t)(slot - base) * p.S + gpx + n16;
+          float* dst = Pl + (size_t)(slot - base) * pitch + gpx + n16;
 #pragma unroll
           for (int t = 0; t < 3; ++t)
             if (gpx + 16 * t + n16 < p.S) dst[16 * t] = TWO ? acc[u][t][i] : w * acc[u][t][i];
@@ -574,9 +686,9 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
         float bv;
         int bi;
         if (p.W <= kWave)
-          expand_row<true, kOutNone>(Pl + (size_t)r * p.S, nullptr, g, lane, true, bv, bi);
+          row_peak<true>(Pl + (size_t)r * pitch, hl, g, lane, bv, bi);
         else
-          expand_row<false, kOutNone>(Pl + (size_t)r * p.S, nullptr, g, lane, true, bv, bi);
+          row_peak<false>(Pl + (size_t)r * pitch, hl, g, lane, bv, bi);
         if (lane == 0)
           write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + s_rows[base + r], bv, bi, g.Ho,
                          g.Wo);

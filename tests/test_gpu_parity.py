@@ -338,6 +338,36 @@ def test_keypoints_only(gkd, ora, dtype, shape):
     check_decode(tuple(t.cpu().numpy() for t in got), oh, valid, dtype, floors=floors_of(q))
 
 
+def test_keypoints_only_ties(gkd):
+    """Keypoints only on maps with exact ties: plateaus of identical feature
+    vectors (a ridge, a block, a 2x2 at a corner, one flat crop) equal the
+    decode of the call with heatmaps, bit for bit. The contraction's peak
+    search evaluates only the neighbourhoods of cells near the maximum and
+    falls back to the full scan on flat maps; either way the first
+    occurrence must win."""
+    B, C, H, W, R = 4, 64, 24, 24, 16
+    rng = np.random.default_rng(91)
+    q = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    kv = rng.standard_normal((B, R, C)).astype(np.float32)
+    v = rng.standard_normal(C).astype(np.float32)
+    kv[:, ::2] = v                           # every other row peaks on the plateaus
+    q[0, :, 7, 2:22] = v[:, None]            # a ridge of 20 cells
+    q[1, :, 10:16, 3:9] = v[:, None, None]   # a 6x6 block (36 cells)
+    q[2, :, 22:, 22:] = v[:, None, None]     # a 2x2 block at the corner
+    q[2, :, 0, 0] = v                        # and a lone cell at the other
+    q[3] = v[:, None, None]                  # flat crop: every cell ties
+    mv = np.ones((B, R), np.uint8)
+    mv[1, 3] = 0
+    q, kv = gkdsynth.round_bf16_f32(q), gkdsynth.round_bf16_f32(kv)
+    print("[kp-only] ties", flush=True)
+    args = (dev_tensor(q, torch.bfloat16), dev_tensor(kv, torch.bfloat16), dev_tensor(mv))
+    _, full = gkd.kernel_heatmap(*args)
+    got = gkd.kernel_heatmap(*args, with_heatmaps=False)
+    torch.cuda.synchronize()
+    for g, f in zip(got, full):
+        assert torch.equal(g.view(torch.int32), f.view(torch.int32))
+
+
 def test_keypoints_only_longtail(gkd):
     """The long-tail batch, keypoints only: equal to the decode of the call
     with heatmaps, bit for bit."""
