@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--workload", default="longtail_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the bf16-heatmap and keypoints-only passes (profiling runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -293,36 +295,55 @@ def main():
     torch.cuda.synchronize()
     vkp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evv]))
 
-    # secondary mode, outside the headline: the same steps with bfloat16
-    # heatmaps (half the bytes of the dominant output stream)
-    heat16 = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.bfloat16, device=dev)
-    n16 = max(20, args.steps // 4)
-    for _ in range(args.warmup):
-        step(bf16_heat=True)
-    ev16 = [[TimingEvent(torch) for _ in range(2)] for _ in range(n16)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(n16):
-        step(ev16[k], bf16_heat=True)
-    torch.cuda.synchronize()
-    ms16 = (time.perf_counter() - t0) * 1e3 / n16
-    hm16 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev16]))
-    heat16_bytes = heat_bytes - rows * 16 * H * W * 2  # 2 of the 4 bytes per heatmap value
-    del heat16
-    heat16 = None
+    modes = None
+    if not args.no_modes:
+        # secondary mode, outside the headline: the same steps with bfloat16
+        # heatmaps (half the bytes of the dominant output stream)
+        heat16 = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.bfloat16, device=dev)
+        n16 = max(20, args.steps // 4)
+        for _ in range(args.warmup):
+            step(bf16_heat=True)
+        ev16 = [[TimingEvent(torch) for _ in range(2)] for _ in range(n16)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(n16):
+            step(ev16[k], bf16_heat=True)
+        torch.cuda.synchronize()
+        ms16 = (time.perf_counter() - t0) * 1e3 / n16
+        hm16 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev16]))
+        heat16_bytes = heat_bytes - rows * 16 * H * W * 2  # 2 of the 4 bytes per heatmap value
+        del heat16
+        heat16 = None
 
-    # and with the keypoints only (no heatmaps at all)
-    for _ in range(args.warmup):
-        step(kp_only=True)
-    evk = [[TimingEvent(torch) for _ in range(2)] for _ in range(n16)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(n16):
-        step(evk[k], kp_only=True)
-    torch.cuda.synchronize()
-    mskp = (time.perf_counter() - t0) * 1e3 / n16
-    hmkp = float(np.mean([e[0].elapsed_time(e[1]) for e in evk]))
-    kp_bytes = heat_bytes - rows * 16 * H * W * 4  # no heatmap bytes
+        # and with the keypoints only (no heatmaps at all)
+        for _ in range(args.warmup):
+            step(kp_only=True)
+        evk = [[TimingEvent(torch) for _ in range(2)] for _ in range(n16)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(n16):
+            step(evk[k], kp_only=True)
+        torch.cuda.synchronize()
+        mskp = (time.perf_counter() - t0) * 1e3 / n16
+        hmkp = float(np.mean([e[0].elapsed_time(e[1]) for e in evk]))
+        kp_bytes = heat_bytes - rows * 16 * H * W * 4  # no heatmap bytes
+        modes = {
+            "heatmap_bf16": {
+                "note": "same workload, heatmaps stored as bfloat16 (GKD_HEATMAP_BF16); "
+                        "not the headline",
+                "steps": n16, "ms_per_step": round(ms16, 4),
+                "heatmaps_per_s": round(rows / (ms16 * 1e-3), 1),
+                "heatmap_call_ms": round(hm16, 4), "heatmap_call_alg_bytes": heat16_bytes,
+                "heatmap_call_gbps": round(heat16_bytes / (hm16 * 1e-3) / 1e9, 1),
+            },
+            "keypoints_only": {
+                "note": "same workload, keypoints only (heatmaps NULL); not the headline",
+                "steps": n16, "ms_per_step": round(mskp, 4),
+                "keypoints_per_s": round(rows / (mskp * 1e-3), 1),
+                "call_ms": round(hmkp, 4), "call_alg_bytes": kp_bytes,
+                "call_gbps": round(kp_bytes / (hmkp * 1e-3) / 1e9, 1),
+            },
+        }
 
     achieved = heat_bytes / (hm_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
@@ -378,23 +399,7 @@ def main():
         "step_hbm_frac": round((heat_bytes + vkp_bytes) / (ms_step * 1e-3) / 1e9
                                / HBM_PEAK_GBS, 4),
         "copy_gbps_measured": round(copy_gbs, 1),
-        "modes": {
-            "heatmap_bf16": {
-                "note": "same workload, heatmaps stored as bfloat16 (GKD_HEATMAP_BF16); "
-                        "not the headline",
-                "steps": n16, "ms_per_step": round(ms16, 4),
-                "heatmaps_per_s": round(rows / (ms16 * 1e-3), 1),
-                "heatmap_call_ms": round(hm16, 4), "heatmap_call_alg_bytes": heat16_bytes,
-                "heatmap_call_gbps": round(heat16_bytes / (hm16 * 1e-3) / 1e9, 1),
-            },
-            "keypoints_only": {
-                "note": "same workload, keypoints only (heatmaps NULL); not the headline",
-                "steps": n16, "ms_per_step": round(mskp, 4),
-                "keypoints_per_s": round(rows / (mskp * 1e-3), 1),
-                "call_ms": round(hmkp, 4), "call_alg_bytes": kp_bytes,
-                "call_gbps": round(kp_bytes / (hmkp * 1e-3) / 1e9, 1),
-            },
-        },
+        "modes": modes,
         "parity": parity,
     }
     print(json.dumps(out), flush=True)
