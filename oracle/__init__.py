@@ -60,6 +60,10 @@ def _load():
         lib.gko_kernel_heatmap.restype = _I
         lib.gko_kernel_heatmap.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I,
                                            _I, _I, _P]
+        lib.gko_roi_preprocess.restype = _I
+        lib.gko_roi_preprocess.argtypes = [_P, _I, _I, _P, _I, _I, _P]
+        lib.gko_roi_backproject.restype = _I
+        lib.gko_roi_backproject.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P]
         lib.gko_peak_decode.restype = _I
         lib.gko_peak_decode.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P,
                                         _P]
@@ -161,3 +165,40 @@ def peak_decode(heat, row_valid=None):
                                _ptr(idx), _ptr(xy), _ptr(score), _ptr(gap)),
            "peak_decode")
     return idx, xy, score, gap
+
+
+def _boxes(boxes):
+    b = np.ascontiguousarray(boxes, dtype=np.int32)
+    if b.ndim != 2 or b.shape[1] != 4:
+        raise ValueError("boxes must be [B, 4]")
+    return b
+
+
+def roi_preprocess(image, boxes, size=384):
+    """image [H, W, 3] uint8 RGB, boxes [B, 4] int (x0, y0, x1, y1) ->
+    [B, 3, size, size] float64: crop, resize the longer side to `size`,
+    centre-pad with the mean colour, ImageNet-normalise."""
+    lib = _load()
+    img = np.ascontiguousarray(image, dtype=np.uint8)
+    if img.ndim != 3 or img.shape[2] != 3:
+        raise ValueError("image must be [H, W, 3]")
+    b = _boxes(boxes)
+    out = np.empty((b.shape[0], 3, size, size), dtype=np.float64)
+    _check(lib.gko_roi_preprocess(_ptr(img), img.shape[0], img.shape[1], _ptr(b),
+                                  b.shape[0], size, _ptr(out)), "roi_preprocess")
+    return out
+
+
+def roi_backproject(xy, boxes, image_hw, size=384):
+    """xy [B, R, 2] in the canvas's -1..1 frame -> image coordinates
+    [B, R, 2] (continuous: pixel i covers [i, i + 1)); NaN for empty boxes."""
+    lib = _load()
+    x = _f64(xy)
+    b = _boxes(boxes)
+    if x.ndim != 3 or x.shape[2] != 2 or x.shape[0] != b.shape[0]:
+        raise ValueError("xy must be [B, R, 2]")
+    out = np.empty_like(x)
+    _check(lib.gko_roi_backproject(_ptr(x), _ptr(b), x.shape[0], x.shape[1],
+                                   int(image_hw[0]), int(image_hw[1]), size, _ptr(out)),
+           "roi_backproject")
+    return out

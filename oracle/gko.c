@@ -300,3 +300,154 @@ int gko_peak_decode(const double *heat, const uint8_t *row_valid, int B,
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* ROI stage either side of the head (model card, section "Model": the     */
+/* Input bullet resizes the image so its longer side is the input size,    */
+/* centre-pads it to a square with the mean colour (124, 116, 104) and     */
+/* applies ImageNet normalisation; the Output bullet gives the keypoints   */
+/* in the ROI's -1..1 frame. Top-down use crops each detector box first).  */
+/*                                                                         */
+/* Readings where the card is silent:                                      */
+/*   - a box is an integer pixel rectangle (x0, y0, x1, y1), x1 and y1     */
+/*     exclusive, clamped to the image; an empty box gives a canvas of     */
+/*     pad colour and NaN back-projections;                                */
+/*   - the resized size: the longer side becomes L, the shorter one is     */
+/*     round(short * L / long), halves rounded up, at least 1 (integers);  */
+/*   - the pad splits with the odd pixel on the right / bottom;            */
+/*   - the resize is bilinear with half-pixel centres and edge clamping    */
+/*     inside the crop (the convention of the head's own upsample), no     */
+/*     antialiasing and no re-quantisation to 8 bits;                      */
+/*   - ImageNet normalisation: (v / 255 - mean_c) / std_c with mean         */
+/*     (0.485, 0.456, 0.406) and std (0.229, 0.224, 0.225), pad included;  */
+/*   - a -1..1 coordinate spans the canvas edge to edge, and image          */
+/*     coordinates are continuous (pixel i covers [i, i + 1)).             */
+/* ---------------------------------------------------------------------- */
+static const double roi_mean[3] = {0.485, 0.456, 0.406};
+static const double roi_std[3] = {0.229, 0.224, 0.225};
+static const double roi_pad[3] = {124.0, 116.0, 104.0};
+
+typedef struct {
+    int x0, y0, bw, bh;   /* clamped box; bw or bh 0 = empty */
+    int nw, nh;           /* resized size */
+    int px, py;           /* left / top pad */
+} roi_geom;
+
+static roi_geom roi_geometry(const int *box, int H, int W, int L)
+{
+    roi_geom g;
+    int x0 = box[0], y0 = box[1], x1 = box[2], y1 = box[3];
+    x0 = x0 < 0 ? 0 : (x0 > W ? W : x0);
+    x1 = x1 < 0 ? 0 : (x1 > W ? W : x1);
+    y0 = y0 < 0 ? 0 : (y0 > H ? H : y0);
+    y1 = y1 < 0 ? 0 : (y1 > H ? H : y1);
+    g.x0 = x0;
+    g.y0 = y0;
+    g.bw = x1 > x0 ? x1 - x0 : 0;
+    g.bh = y1 > y0 ? y1 - y0 : 0;
+    g.nw = g.nh = g.px = g.py = 0;
+    if (g.bw == 0 || g.bh == 0) {
+        g.bw = g.bh = 0;
+        return g;
+    }
+    const long lng = g.bw > g.bh ? g.bw : g.bh;
+    /* round(side * L / long), halves up, in exact integers */
+    g.nw = (int)(((long)2 * g.bw * L + lng) / ((long)2 * lng));
+    g.nh = (int)(((long)2 * g.bh * L + lng) / ((long)2 * lng));
+    if (g.nw < 1) g.nw = 1;
+    if (g.nh < 1) g.nh = 1;
+    g.px = (L - g.nw) / 2;
+    g.py = (L - g.nh) / 2;
+    return g;
+}
+
+/* Source taps of output sample o when n_in samples are resized to n_out:
+ * half-pixel centres, negative positions clamped to 0, upper tap clamped. */
+static void resize_taps(int o, int n_in, int n_out, int *i0, int *i1, double *lam)
+{
+    double src = ((double)o + 0.5) * ((double)n_in / (double)n_out) - 0.5;
+    if (src < 0.0) src = 0.0;
+    int a = (int)floor(src);
+    if (a > n_in - 1) a = n_in - 1;
+    *i0 = a;
+    *i1 = a + 1 < n_in ? a + 1 : n_in - 1;
+    *lam = src - (double)a;
+}
+
+/* image [H,W,3] uint8 RGB, boxes [B,4]; out [B,3,L,L]. */
+int gko_roi_preprocess(const uint8_t *image, int H, int W, const int *boxes,
+                       int B, int L, double *out)
+{
+    if (H < 1 || W < 1 || B < 0 || L < 1) return 2;
+    const long LL = (long)L * L;
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        const roi_geom g = roi_geometry(boxes + 4 * b, H, W, L);
+        /* 1. the canvas starts as the pad colour */
+        double *canvas = malloc(sizeof(double) * 3 * LL);
+        for (long p = 0; p < LL; ++p)
+            for (int c = 0; c < 3; ++c) canvas[3 * p + c] = roi_pad[c];
+        if (g.bw > 0) {
+            /* 2. crop the box */
+            double *crop = malloc(sizeof(double) * 3 * (long)g.bw * g.bh);
+            for (int y = 0; y < g.bh; ++y)
+                for (int x = 0; x < g.bw; ++x)
+                    for (int c = 0; c < 3; ++c)
+                        crop[3 * ((long)y * g.bw + x) + c] =
+                            image[3 * ((long)(g.y0 + y) * W + g.x0 + x) + c];
+            /* 3. resize it to nh x nw and paste it centred */
+            for (int v = 0; v < g.nh; ++v) {
+                int r0, r1;
+                double ly;
+                resize_taps(v, g.bh, g.nh, &r0, &r1, &ly);
+                for (int u = 0; u < g.nw; ++u) {
+                    int s0, s1;
+                    double lx;
+                    resize_taps(u, g.bw, g.nw, &s0, &s1, &lx);
+                    for (int c = 0; c < 3; ++c) {
+                        const double a = crop[3 * ((long)r0 * g.bw + s0) + c];
+                        const double bq = crop[3 * ((long)r0 * g.bw + s1) + c];
+                        const double cq = crop[3 * ((long)r1 * g.bw + s0) + c];
+                        const double d = crop[3 * ((long)r1 * g.bw + s1) + c];
+                        const double top = (1.0 - lx) * a + lx * bq;
+                        const double bot = (1.0 - lx) * cq + lx * d;
+                        canvas[3 * ((long)(g.py + v) * L + g.px + u) + c] =
+                            (1.0 - ly) * top + ly * bot;
+                    }
+                }
+            }
+            free(crop);
+        }
+        /* 4. ImageNet normalisation, channels first */
+        for (int c = 0; c < 3; ++c)
+            for (long p = 0; p < LL; ++p)
+                out[(long)b * 3 * LL + (long)c * LL + p] =
+                    (canvas[3 * p + c] / 255.0 - roi_mean[c]) / roi_std[c];
+        free(canvas);
+    }
+    return 0;
+}
+
+/* xy [B,R,2] in the canvas's -1..1 frame -> image coordinates [B,R,2]:
+ * the canvas position (x + 1) L / 2, less the pad, scaled back by the
+ * crop's size over the resized size, plus the box origin. */
+int gko_roi_backproject(const double *xy, const int *boxes, int B, int R,
+                        int H, int W, int L, double *out)
+{
+    if (H < 1 || W < 1 || B < 0 || R < 0 || L < 1) return 2;
+    for (int b = 0; b < B; ++b) {
+        const roi_geom g = roi_geometry(boxes + 4 * b, H, W, L);
+        for (int r = 0; r < R; ++r) {
+            const long o = 2 * ((long)b * R + r);
+            if (g.bw == 0) {
+                out[o] = out[o + 1] = NAN;
+                continue;
+            }
+            const double xc = (xy[o] + 1.0) * L / 2.0;
+            const double yc = (xy[o + 1] + 1.0) * L / 2.0;
+            out[o] = g.x0 + (xc - g.px) * ((double)g.bw / g.nw);
+            out[o + 1] = g.y0 + (yc - g.py) * ((double)g.bh / g.nh);
+        }
+    }
+    return 0;
+}
