@@ -28,5 +28,6 @@ Recipe (every config):
   * dual rows plant along unit(u_r + unit(k_txt)).
 """
 from .configs import CONFIGS, config_names, make, round_bf16_f32, bf16_bits
+from .roi import make_roi
 
-__all__ = ["CONFIGS", "config_names", "make", "round_bf16_f32", "bf16_bits"]
+__all__ = ["CONFIGS", "config_names", "make", "make_roi", "round_bf16_f32", "bf16_bits"]

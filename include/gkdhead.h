@@ -12,7 +12,11 @@
  *                         features, fused per row over the prompt modalities,
  *                         optionally with the peak decode fused in;
  *   3. gkd_peak_decode    per-row argmax of a heatmap, mapped to -1..1, plus
- *                         the score.
+ *                         the score;
+ * and the ROI stage either side of the head in top-down use:
+ *   4. gkd_roi_preprocess   crop, resize, centre-pad and normalise detector
+ *                           boxes of an image into the backbone's input;
+ *   5. gkd_roi_backproject  -1..1 keypoints back to image coordinates.
  *
  * Conventions shared by every call:
  *   - Every array argument is a DEVICE pointer owned by the caller, dense
@@ -37,7 +41,8 @@
  *
  * ABI history: version 1 had float32 heatmaps only; version 2 adds
  * GKD_HEATMAP_BF16 (gkd_kernel_heatmap's heatmaps argument became void *,
- * which existing callers pass unchanged).
+ * which existing callers pass unchanged); version 3 adds the ROI stage
+ * (gkd_roi_preprocess, gkd_roi_backproject).
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -49,7 +54,7 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 2
+#define GKD_ABI_VERSION 3
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
@@ -186,6 +191,61 @@ GKD_API gkd_status gkd_peak_decode(const float *heatmaps, const uint8_t *row_val
                            int B, int R, int Ho, int Wo, uint32_t flags,
                            int32_t *peak_idx, float *peak_xy,
                            float *peak_score, hipStream_t stream);
+
+/*
+ * ROI preprocessing.
+ * GKDT-L GGUF model card, section "Model", "Input" bullet: the image is
+ * resized so that its longer side is the input size, centre-padded to a
+ * square with the mean colour (124, 116, 104), and ImageNet-normalised;
+ * in top-down use (GKDT paper summary, agihunt.info: keypoints per
+ * detected object) each detector box is cropped first. Conventions the
+ * card leaves open:
+ *   - a box is an integer pixel rectangle (x0, y0, x1, y1), x1 and y1
+ *     exclusive, clamped to the image; an empty box (after clamping) gives
+ *     a canvas of pad colour;
+ *   - the box's longer side becomes out_size, the shorter one
+ *     round(side * out_size / longer), halves up, at least 1;
+ *   - the resized crop sits at ((out_size - nw) / 2, (out_size - nh) / 2)
+ *     (integer division: an odd pixel of pad goes right / bottom);
+ *   - the resize is bilinear with half-pixel centres (source position
+ *     (u + 1/2) bw / nw - 1/2, clamped below at 0; the upper tap clamps at
+ *     the crop's last pixel), without antialiasing and without rounding
+ *     back to 8 bits;
+ *   - every canvas value v (pad included) becomes
+ *     (v / 255 - mean_c) / std_c, mean (0.485, 0.456, 0.406),
+ *     std (0.229, 0.224, 0.225), c = R, G, B.
+ * The arithmetic is float32; taps and their fractions come from exact
+ * integer ratios.
+ *
+ *   image     [height,width,3] uint8 RGB (no alignment requirement)
+ *   boxes     [B,4] int32, 4-byte aligned (any values: they are clamped)
+ *   out       [B,3,out_size,out_size] dtype (float32 or bfloat16, rounded
+ *             to nearest even), 16-byte aligned
+ * Limits: 1 <= height, width <= 65535; 1 <= out_size <= 4096;
+ * B <= 65535 (else GKD_ERR_SHAPE).
+ */
+GKD_API gkd_status gkd_roi_preprocess(const uint8_t *image, int height, int width,
+                              const int32_t *boxes, int B, int out_size,
+                              gkd_dtype dtype, uint32_t flags, void *out,
+                              hipStream_t stream);
+
+/*
+ * ROI back-projection.
+ * GKDT-L GGUF model card, section "Model", "Output" bullet: keypoints come
+ * out in the ROI's normalised -1..1 frame. This maps them to the image:
+ *   x_img = x0 + ((x + 1) out_size / 2 - px) * bw / nw
+ * and the same along y, with the box geometry of gkd_roi_preprocess; image
+ * coordinates are continuous (pixel i covers [i, i + 1)). NaN inputs (the
+ * decode's invalid rows) stay NaN; empty boxes give NaN.
+ *
+ *   xy        [B,R,2] float32, 4-byte aligned
+ *   boxes     [B,4] int32, the boxes given to gkd_roi_preprocess
+ *   out_xy    [B,R,2] float32, 4-byte aligned
+ * Limits: as gkd_roi_preprocess.
+ */
+GKD_API gkd_status gkd_roi_backproject(const float *xy, const int32_t *boxes, int B,
+                               int R, int height, int width, int out_size,
+                               uint32_t flags, float *out_xy, hipStream_t stream);
 
 #ifdef __cplusplus
 }

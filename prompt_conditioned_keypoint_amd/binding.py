@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
-GKD_ABI_VERSION = 2          # include/gkdhead.h
+GKD_ABI_VERSION = 3          # include/gkdhead.h
 GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
 STATUS = {0: "GKD_OK", 1: "GKD_ERR_NULL", 2: "GKD_ERR_SHAPE", 3: "GKD_ERR_DTYPE",
           4: "GKD_ERR_VALUE", 5: "GKD_ERR_UNSUPPORTED", 6: "GKD_ERR_HIP",
@@ -57,6 +57,10 @@ def load():
                                        _U32, _P, _P, _P, _P, _P]
     lib.gkd_peak_decode.restype = _I
     lib.gkd_peak_decode.argtypes = [_P, _P, _I, _I, _I, _I, _U32, _P, _P, _P, _P]
+    lib.gkd_roi_preprocess.restype = _I
+    lib.gkd_roi_preprocess.argtypes = [_P, _I, _I, _P, _I, _I, _I, _U32, _P, _P]
+    lib.gkd_roi_backproject.restype = _I
+    lib.gkd_roi_backproject.argtypes = [_P, _P, _I, _I, _I, _I, _I, _U32, _P, _P]
     if lib.gkd_abi_version() != GKD_ABI_VERSION:
         raise ImportError("libgkdhead ABI version mismatch")
     _lib = lib
@@ -198,3 +202,50 @@ def peak_decode(heat: torch.Tensor, row_valid: torch.Tensor | None = None):
     _check(lib.gkd_peak_decode(_ptr(heat), _ptr(row_valid), B, R, Ho, Wo, 0, _ptr(idx),
                                _ptr(xy), _ptr(score), _stream(heat.device)))
     return idx, xy, score
+
+
+def roi_preprocess(image: torch.Tensor, boxes: torch.Tensor, size: int = 384,
+                   dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    """image [H,W,3] u8 RGB, boxes [B,4] i32 (x0, y0, x1, y1) -> the
+    backbone input [B,3,size,size] in dtype (float32 or bfloat16): each box
+    cropped, resized so its longer side is `size`, centre-padded with the
+    mean colour and ImageNet-normalised."""
+    lib = load()
+    _dev(image, "image", torch.uint8, 3)
+    _dev(boxes, "boxes", torch.int32, 2)
+    if image.shape[2] != 3 or boxes.shape[1] != 4:
+        raise ValueError("image must be [H,W,3] and boxes [B,4]")
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("dtype must be float32 or bfloat16")
+    B = boxes.shape[0]
+    if out is None:
+        out = torch.empty((B, 3, size, size), dtype=dtype, device=image.device)
+    else:
+        _dev(out, "out", dtype, 4)
+        if out.shape != (B, 3, size, size):
+            raise ValueError("out must be [B,3,size,size]")
+    _check(lib.gkd_roi_preprocess(_ptr(image), image.shape[0], image.shape[1], _ptr(boxes), B,
+                                  size, 1 if dtype == torch.bfloat16 else 0, 0, _ptr(out),
+                                  _stream(image.device)))
+    return out
+
+
+def roi_backproject(xy: torch.Tensor, boxes: torch.Tensor, image_hw, size: int = 384,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """xy [B,R,2] f32 in the ROI canvas's -1..1 frame -> image coordinates
+    [B,R,2] f32 (continuous, pixel i covers [i, i + 1)); NaN stays NaN."""
+    lib = load()
+    _dev(xy, "xy", torch.float32, 3)
+    _dev(boxes, "boxes", torch.int32, 2)
+    B, R, two = xy.shape
+    if two != 2 or boxes.shape != (B, 4):
+        raise ValueError("xy must be [B,R,2] and boxes [B,4]")
+    if out is None:
+        out = torch.empty_like(xy)
+    else:
+        _dev(out, "out", torch.float32, 3)
+        if out.shape != xy.shape:
+            raise ValueError("out must be [B,R,2]")
+    _check(lib.gkd_roi_backproject(_ptr(xy), _ptr(boxes), B, R, int(image_hw[0]),
+                                   int(image_hw[1]), size, 0, _ptr(out), _stream(xy.device)))
+    return out

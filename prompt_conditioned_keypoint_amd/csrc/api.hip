@@ -188,4 +188,66 @@ gkd_status gkd_peak_decode(const float* heatmaps, const uint8_t* row_valid, int 
   return hip_status(gkd::launch_decode(a, stream), "gkd_peak_decode");
 }
 
+namespace {
+
+gkd_status roi_shape(const char* fn, int H, int W, int B, int L) {
+  if (H < 1 || W < 1 || H > 65535 || W > 65535 || B < 0 || B > 65535 || L < 1 || L > 4096)
+    return fail(GKD_ERR_SHAPE, "%s: bad shape height=%d width=%d B=%d out_size=%d", fn, H, W, B,
+                L);
+  if ((long long)H * W * 3 > kMaxElems || (long long)B * 3 * L * L > kMaxElems)
+    return fail(GKD_ERR_SHAPE, "%s: an element count reaches 2^31", fn);
+  return GKD_OK;
+}
+
+}  // namespace
+
+gkd_status gkd_roi_preprocess(const uint8_t* image, int height, int width, const int32_t* boxes,
+                              int B, int out_size, gkd_dtype dtype, uint32_t flags, void* out,
+                              hipStream_t stream) {
+  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_roi_preprocess: flags must be 0");
+  if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
+    return fail(GKD_ERR_DTYPE, "gkd_roi_preprocess: unknown dtype %d", (int)dtype);
+  const gkd_status sh = roi_shape("gkd_roi_preprocess", height, width, B, out_size);
+  if (sh != GKD_OK) return sh;
+  if (B == 0) return ok();
+  if (!image || !boxes || !out) return fail(GKD_ERR_NULL, "gkd_roi_preprocess: NULL pointer argument");
+  if (!aligned4(boxes) || !aligned16(out))
+    return fail(GKD_ERR_ALIGN, "gkd_roi_preprocess: boxes need 4-byte, out 16-byte alignment");
+  gkd::RoiArgs a;
+  a.image = image;
+  a.H = height;
+  a.W = width;
+  a.boxes = boxes;
+  a.B = B;
+  a.L = out_size;
+  a.bf16 = dtype == GKD_DTYPE_BF16;
+  a.out = out;
+  return hip_status(gkd::launch_roi(a, stream), "gkd_roi_preprocess");
+}
+
+gkd_status gkd_roi_backproject(const float* xy, const int32_t* boxes, int B, int R, int height,
+                               int width, int out_size, uint32_t flags, float* out_xy,
+                               hipStream_t stream) {
+  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_roi_backproject: flags must be 0");
+  const gkd_status sh = roi_shape("gkd_roi_backproject", height, width, B, out_size);
+  if (sh != GKD_OK) return sh;
+  if (R < 0) return fail(GKD_ERR_SHAPE, "gkd_roi_backproject: bad shape R=%d", R);
+  if ((long long)B * R * 2 > kMaxElems)
+    return fail(GKD_ERR_SHAPE, "gkd_roi_backproject: an element count reaches 2^31");
+  if (B == 0 || R == 0) return ok();
+  if (!xy || !boxes || !out_xy) return fail(GKD_ERR_NULL, "gkd_roi_backproject: NULL pointer argument");
+  if (!aligned4(xy) || !aligned4(boxes) || !aligned4(out_xy))
+    return fail(GKD_ERR_ALIGN, "gkd_roi_backproject: arrays need 4-byte alignment");
+  gkd::BackprojectArgs a;
+  a.xy = xy;
+  a.boxes = boxes;
+  a.B = B;
+  a.R = R;
+  a.H = height;
+  a.W = width;
+  a.L = out_size;
+  a.out = out_xy;
+  return hip_status(gkd::launch_backproject(a, stream), "gkd_roi_backproject");
+}
+
 }  // extern "C"

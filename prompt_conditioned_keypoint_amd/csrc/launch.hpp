@@ -41,6 +41,22 @@ struct DecodeArgs {
   float* score;
 };
 
+struct RoiArgs {
+  const uint8_t* image;   // [H,W,3] RGB
+  int H, W;
+  const int32_t* boxes;   // [B,4] (x0, y0, x1, y1)
+  int B, L;
+  bool bf16;
+  void* out;              // [B,3,L,L]
+};
+
+struct BackprojectArgs {
+  const float* xy;        // [B,R,2] in the canvas's -1..1 frame
+  const int32_t* boxes;
+  int B, R, H, W, L;
+  float* out;             // [B,R,2] image coordinates
+};
+
 // Shape limits of the heatmap kernel: its LDS holds the fused low-res maps
 // of at least one row (S floats).
 constexpr int kHeatmapMaxS = 16384;
@@ -69,5 +85,7 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps);
 hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream);
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_roi(const RoiArgs& a, hipStream_t stream);
+hipError_t launch_backproject(const BackprojectArgs& a, hipStream_t stream);
 
 }  // namespace gkd

@@ -46,13 +46,14 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"gkd_vkp_pool", "gkd_kernel_heatmap", "gkd_peak_decode"} <= set(names)
+    assert {"gkd_vkp_pool", "gkd_kernel_heatmap", "gkd_peak_decode", "gkd_roi_preprocess",
+            "gkd_roi_backproject"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 2
+    assert lib.gkd_abi_version() == 3
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
@@ -161,6 +162,58 @@ def test_peak_decode_rejects(lib, kw, status):
 
 def test_peak_decode_empty_batch_is_ok(lib):
     assert dec(lib, R=0, heat=None) == OK
+
+
+def roi(lib, image=A, H=1080, W=1920, boxes=A2, B=4, L=384, dtype=0, flags=0, out=A3):
+    return lib.gkd_roi_preprocess(image, H, W, boxes, B, L, dtype, flags, out, None)
+
+
+def bp(lib, xy=A, boxes=A2, B=4, R=80, H=1080, W=1920, L=384, flags=0, out=A3):
+    return lib.gkd_roi_backproject(xy, boxes, B, R, H, W, L, flags, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=1), UNSUP),
+    (dict(dtype=2), DTYPE),
+    (dict(H=0), SHAPE),
+    (dict(W=65536), SHAPE),
+    (dict(B=-1), SHAPE),
+    (dict(B=65536), SHAPE),
+    (dict(L=0), SHAPE),
+    (dict(L=4097), SHAPE),
+    (dict(B=5000, L=4096), SHAPE),            # B*3*L*L >= 2^31
+    (dict(image=None), NULL),
+    (dict(boxes=None), NULL),
+    (dict(out=None), NULL),
+    (dict(boxes=A2 + 2), ALIGN),
+    (dict(out=A3 + 8), ALIGN),
+])
+def test_roi_preprocess_rejects(lib, kw, status):
+    assert roi(lib, **kw) == status
+    assert lib.gkd_last_error().decode() != ""
+
+
+def test_roi_preprocess_empty_batch_is_ok(lib):
+    assert roi(lib, B=0, image=None, boxes=None, out=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=2), UNSUP),
+    (dict(R=-1), SHAPE),
+    (dict(H=-1), SHAPE),
+    (dict(L=5000), SHAPE),
+    (dict(B=60000, R=20000), SHAPE),           # B*R*2 >= 2^31
+    (dict(xy=None), NULL),
+    (dict(out=None), NULL),
+    (dict(xy=A + 1), ALIGN),
+    (dict(boxes=A2 + 2), ALIGN),
+])
+def test_roi_backproject_rejects(lib, kw, status):
+    assert bp(lib, **kw) == status
+
+
+def test_roi_backproject_empty_is_ok(lib):
+    assert bp(lib, R=0, xy=None, boxes=None, out=None) == OK
 
 
 def test_last_error_is_thread_local(lib):
