@@ -18,6 +18,8 @@ workload on this host.
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --copy-only      # plain copy kernel of known size, for
                                    # scaling rocprofv3 byte counters
+  python bench.py --no-modes       # headline only (profiling runs)
+  python bench.py --roi-only       # the ROI stage only (profiling runs)
 """
 from __future__ import annotations
 
@@ -194,6 +196,60 @@ def check_parity(d, heat_gpu, dec_gpu, ora_heat):
                 argmax_mismatch=bad, ok=bool(worst <= 2e-2 and bad == 0))
 
 
+def roi_stage(torch, gkd, n=50, with_cpu=True):
+    """The ROI stage on its own workload (256 detector boxes on a 1920x1080
+    8-bit image -> [256, 3, 384, 384]): gkd_roi_preprocess in float32 and
+    bfloat16, rated by its algorithmic bytes (the canvas written once, the
+    image and boxes read once) over its event-timed duration, and
+    gkd_roi_backproject of 80 keypoints per box."""
+    import gkdsynth
+    d = gkdsynth.make_roi()
+    dev = "cuda"
+    img = torch.from_numpy(d["image"]).to(dev)
+    boxes = torch.from_numpy(d["boxes"]).to(dev)
+    xy = torch.from_numpy(d["xy"]).to(dev)
+    B, L = d["B"], d["size"]
+    res = {"note": "ROI stage: 256 detector boxes on a 1920x1080 RGB image -> "
+                   "[256,3,384,384]; not the headline",
+           "workload": {"B": B, "image": [d["H"], d["W"]], "size": L}}
+    for name, dt, e in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        out = torch.empty((B, 3, L, L), dtype=dt, device=dev)
+        for _ in range(5):
+            gkd.roi_preprocess(img, boxes, size=L, dtype=dt, out=out)
+        evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for k in range(n):
+            evs[k][0].record()
+            gkd.roi_preprocess(img, boxes, size=L, dtype=dt, out=out)
+            evs[k][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        nbytes = B * 3 * L * L * e + d["H"] * d["W"] * 3 + B * 16
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "boxes_per_s": round(B / (ms * 1e-3), 1),
+                     "alg_bytes": nbytes, "gbps": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del out
+    out = torch.empty_like(xy)
+    evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        evs[k][0].record()
+        gkd.roi_backproject(xy, boxes, (d["H"], d["W"]), size=L, out=out)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    res["backproject_ms"] = round(float(np.mean([a.elapsed_time(b) for a, b in evs])), 4)
+    if with_cpu:
+        import oracle
+        k = 8
+        t0 = time.perf_counter()
+        oracle.roi_preprocess(d["image"], d["boxes"][:k], size=L)
+        sec = time.perf_counter() - t0
+        res["cpu_oracle"] = {"boxes_per_s": round(k / sec, 2), "sample": f"first {k} boxes",
+                             "cores": oracle.max_threads()}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +258,8 @@ def main():
     ap.add_argument("--workload", default="longtail_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true")
+    ap.add_argument("--roi-only", action="store_true",
+                    help="time only the ROI stage and print its JSON (profiling runs)")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the bf16-heatmap and keypoints-only passes (profiling runs)")
     args = ap.parse_args()
@@ -221,6 +279,9 @@ def main():
     import gkdsynth
     import prompt_conditioned_keypoint_amd as gkd
     gkd.load()
+    if args.roi_only:
+        print(json.dumps(roi_stage(torch, gkd, n=args.steps, with_cpu=False)), flush=True)
+        return
 
     log(f"[bench] generating workload {args.workload}")
     d = gkdsynth.make(args.workload)
@@ -327,7 +388,10 @@ def main():
         mskp = (time.perf_counter() - t0) * 1e3 / n16
         hmkp = float(np.mean([e[0].elapsed_time(e[1]) for e in evk]))
         kp_bytes = heat_bytes - rows * 16 * H * W * 4  # no heatmap bytes
+        log("[bench] ROI stage")
+        roi = roi_stage(torch, gkd, with_cpu=not args.no_cpu_baseline)
         modes = {
+            "roi_stage": roi,
             "heatmap_bf16": {
                 "note": "same workload, heatmaps stored as bfloat16 (GKD_HEATMAP_BF16); "
                         "not the headline",

@@ -217,7 +217,7 @@ GKD_API gkd_status gkd_peak_decode(const float *heatmaps, const uint8_t *row_val
  * The arithmetic is float32; taps and their fractions come from exact
  * integer ratios.
  *
- *   image     [height,width,3] uint8 RGB (no alignment requirement)
+ *   image     [height,width,3] uint8 RGB, 4-byte aligned
  *   boxes     [B,4] int32, 4-byte aligned (any values: they are clamped)
  *   out       [B,3,out_size,out_size] dtype (float32 or bfloat16, rounded
  *             to nearest even), 16-byte aligned

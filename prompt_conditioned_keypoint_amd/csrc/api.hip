@@ -211,8 +211,9 @@ gkd_status gkd_roi_preprocess(const uint8_t* image, int height, int width, const
   if (sh != GKD_OK) return sh;
   if (B == 0) return ok();
   if (!image || !boxes || !out) return fail(GKD_ERR_NULL, "gkd_roi_preprocess: NULL pointer argument");
-  if (!aligned4(boxes) || !aligned16(out))
-    return fail(GKD_ERR_ALIGN, "gkd_roi_preprocess: boxes need 4-byte, out 16-byte alignment");
+  if (!aligned4(image) || !aligned4(boxes) || !aligned16(out))
+    return fail(GKD_ERR_ALIGN,
+                "gkd_roi_preprocess: image and boxes need 4-byte, out 16-byte alignment");
   gkd::RoiArgs a;
   a.image = image;
   a.H = height;

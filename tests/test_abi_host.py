@@ -187,6 +187,7 @@ def bp(lib, xy=A, boxes=A2, B=4, R=80, H=1080, W=1920, L=384, flags=0, out=A3):
     (dict(out=None), NULL),
     (dict(boxes=A2 + 2), ALIGN),
     (dict(out=A3 + 8), ALIGN),
+    (dict(image=A + 2), ALIGN),
 ])
 def test_roi_preprocess_rejects(lib, kw, status):
     assert roi(lib, **kw) == status
