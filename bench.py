@@ -166,7 +166,19 @@ def cpu_baseline(d, target_s=20.0, max_crops=None):
         rows += int(((mv | mt) > 0).sum())
         crops += 1
     dt = time.perf_counter() - t0
-    return rows / dt, dict(crops=crops, rows=rows, seconds=dt), res
+    # and one crop on one host thread
+    nthreads = oracle.max_threads()
+    oracle.set_threads(1)
+    t1 = time.perf_counter()
+    mv, mt = d["mask_vis"][:1], d["mask_txt"][:1]
+    kv = (oracle.vkp_pool(d["support"][:1], d["kpts"][:1], mv, d["stride"], d["sigma"],
+                          dtype=d["dtype"]) if mv.any() else None)
+    oracle.kernel_heatmap(d["query"][:1], kv, mv if mv.any() else None,
+                          d["kern_txt"][:1] if mt.any() else None, mt if mt.any() else None)
+    one = time.perf_counter() - t1
+    oracle.set_threads(nthreads)
+    return rows / dt, dict(crops=crops, rows=rows, seconds=dt, one_crop_1thread_s=one,
+                           one_crop_rows=int(((mv | mt) > 0).sum())), res
 
 
 def check_parity(d, heat_gpu, dec_gpu, ora_heat):
@@ -465,7 +477,9 @@ def main():
                "cores": oracle.max_threads(), "kind": "oracle",
                "sample": (f"first {sample['crops']} crops of the {args.workload} batch "
                           f"({sample['rows']} heatmaps, VKP + heatmap chain, "
-                          f"{sample['seconds']:.1f} s)")}
+                          f"{sample['seconds']:.1f} s)"),
+               "one_crop_one_thread_s": round(sample["one_crop_1thread_s"], 3),
+               "one_crop_rows": sample["one_crop_rows"]}
         # parity of the timed outputs on the sampled crops (the oracle chain
         # uses its own prototypes, so this is an end-to-end check)
         hg = heat.cpu().numpy()

@@ -50,6 +50,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.gko_version.restype = _I
         lib.gko_max_threads.restype = _I
+        lib.gko_set_threads.restype = None
+        lib.gko_set_threads.argtypes = [_I]
         lib.gko_round_bf16.restype = _D
         lib.gko_round_bf16.argtypes = [_D]
         lib.gko_vkp_pool.restype = _I
@@ -90,6 +92,11 @@ def _check(rc, what):
 
 def max_threads() -> int:
     return _load().gko_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the following calls (timing only)."""
+    _load().gko_set_threads(int(n))
 
 
 def round_bf16(x):

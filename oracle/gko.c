@@ -62,6 +62,12 @@ int gko_max_threads(void)
 #endif
 }
 
+/* Set the OpenMP thread count of the following calls (timing only). */
+void gko_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
+
 /* Round a double to the nearest bfloat16 value (8 significant bits,
  * float32 exponent range), ties to even. Finite inputs only; results
  * beyond the bfloat16 range become +-inf. */
