@@ -37,12 +37,15 @@
  *   - Every element count (e.g. B*R*4H*4W) must be below 2^31.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
  *   - `flags` must be 0 (else GKD_ERR_UNSUPPORTED), except for the
- *     heatmap output format flag of gkd_kernel_heatmap (GKD_HEATMAP_BF16).
+ *     heatmap output format flag of gkd_kernel_heatmap (GKD_HEATMAP_BF16)
+ *     and the keypoint coordinate flag of gkd_kernel_heatmap and
+ *     gkd_peak_decode (GKD_COORDS_CORNERS).
  *
  * ABI history: version 1 had float32 heatmaps only; version 2 adds
  * GKD_HEATMAP_BF16 (gkd_kernel_heatmap's heatmaps argument became void *,
  * which existing callers pass unchanged); version 3 adds the ROI stage
- * (gkd_roi_preprocess, gkd_roi_backproject).
+ * (gkd_roi_preprocess, gkd_roi_backproject); version 4 adds
+ * GKD_COORDS_CORNERS.
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -54,11 +57,15 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 3
+#define GKD_ABI_VERSION 4
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
 #define GKD_HEATMAP_BF16 0x1u
+/* gkd_kernel_heatmap and gkd_peak_decode flag: map the peak index to -1..1
+ * corner-aligned, x = 2 col / (Wo - 1) - 1 (0 when Wo == 1), instead of
+ * the cell centre (2 col + 1) / Wo - 1; likewise y. */
+#define GKD_COORDS_CORNERS 0x4u
 
 #ifndef GKD_API
 #define GKD_API __attribute__((visibility("default")))
@@ -158,7 +165,8 @@ GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
  *   peak_xy    [B,R,2] float32   all three NULL = no decode, else all three
  *   peak_score [B,R]   float32   non-NULL. Rows with no mask get the sentinel.
  *                                heatmaps and the decode outputs cannot all
- *                                be NULL (GKD_ERR_NULL).
+ *                                be NULL (GKD_ERR_NULL). GKD_COORDS_CORNERS
+ *                                selects the corner-aligned coordinates.
  * Limits: C >= 1, H >= 1, W >= 1, H*W <= 16384 (else GKD_ERR_UNSUPPORTED).
  */
 GKD_API gkd_status gkd_kernel_heatmap(const void *query, const void *kern_vis,
@@ -178,7 +186,8 @@ GKD_API gkd_status gkd_kernel_heatmap(const void *query, const void *kern_vis,
  * For every (b, r) with row_valid[b,r] != 0 (or every row if row_valid is
  * NULL): p = the lowest flat index y*Wo + x holding the row's maximum;
  *   peak_idx   = p
- *   peak_xy    = ((2x + 1)/Wo - 1, (2y + 1)/Ho - 1)   (cell centres)
+ *   peak_xy    = ((2x + 1)/Wo - 1, (2y + 1)/Ho - 1)   (cell centres), or with
+ *                flags = GKD_COORDS_CORNERS (2x/(Wo - 1) - 1, 2y/(Ho - 1) - 1)
  *   peak_score = heatmaps[b,r,y,x]
  * Invalid rows get idx -1, xy NaN, score -inf.
  *

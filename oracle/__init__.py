@@ -67,8 +67,8 @@ def _load():
         lib.gko_roi_backproject.restype = _I
         lib.gko_roi_backproject.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P]
         lib.gko_peak_decode.restype = _I
-        lib.gko_peak_decode.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P,
-                                        _P]
+        lib.gko_peak_decode.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P,
+                                        _P, _P]
         _lib = lib
     return _lib
 
@@ -157,10 +157,11 @@ def kernel_heatmap(query, kern_vis=None, mask_vis=None, kern_txt=None,
     return out
 
 
-def peak_decode(heat, row_valid=None):
+def peak_decode(heat, row_valid=None, corners=False):
     """heat [B,R,Ho,Wo] -> (idx int32 [B,R], xy [B,R,2], score [B,R],
     gap [B,R]); the values are compared in float64, so pass the heatmap
-    already rounded to the precision the decision is taken in."""
+    already rounded to the precision the decision is taken in. corners:
+    corner-aligned -1..1 coordinates instead of cell centres."""
     lib = _load()
     h = _f64(heat)
     B, R, Ho, Wo = h.shape
@@ -169,7 +170,8 @@ def peak_decode(heat, row_valid=None):
     score = np.empty((B, R))
     gap = np.empty((B, R))
     _check(lib.gko_peak_decode(_ptr(h), _ptr(_u8(row_valid)), B, R, Ho, Wo,
-                               _ptr(idx), _ptr(xy), _ptr(score), _ptr(gap)),
+                               1 if corners else 0, _ptr(idx), _ptr(xy), _ptr(score),
+                               _ptr(gap)),
            "peak_decode")
     return idx, xy, score, gap
 

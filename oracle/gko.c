@@ -274,10 +274,19 @@ int gko_kernel_heatmap(const double *query, const double *kern_vis,
 /* heat [B,R,Ho,Wo]; row_valid [B,R] or NULL (all rows valid).             */
 /* Invalid rows: idx -1, xy NaN, score -inf, gap NaN.                      */
 /* gap = best - max over all other cells (+inf for a 1-cell map).          */
+/* corners: the index maps to -1..1 with the first and last cell at -1 and */
+/* +1 (the convention of align_corners=True grids; 0 for a 1-cell axis)     */
+/* instead of the cell centres.                                            */
 /* ---------------------------------------------------------------------- */
+static double index_coord(long i, int n, int corners)
+{
+    if (!corners) return (2.0 * (double)i + 1.0) / n - 1.0;
+    return n > 1 ? 2.0 * (double)i / (n - 1) - 1.0 : 0.0;
+}
+
 int gko_peak_decode(const double *heat, const uint8_t *row_valid, int B,
-                    int R, int Ho, int Wo, int32_t *idx, double *xy,
-                    double *score, double *gap)
+                    int R, int Ho, int Wo, int corners, int32_t *idx,
+                    double *xy, double *score, double *gap)
 {
     if (B < 0 || R < 0 || Ho < 1 || Wo < 1) return 2;
     const long P = (long)Ho * Wo;
@@ -299,8 +308,8 @@ int gko_peak_decode(const double *heat, const uint8_t *row_valid, int B,
         for (long p = 0; p < P; ++p)
             if (p != best && h[p] > second) second = h[p];
         idx[br] = (int32_t)best;
-        xy[2 * br] = (2.0 * (double)(best % Wo) + 1.0) / Wo - 1.0;
-        xy[2 * br + 1] = (2.0 * (double)(best / Wo) + 1.0) / Ho - 1.0;
+        xy[2 * br] = index_coord(best % Wo, Wo, corners);
+        xy[2 * br + 1] = index_coord(best / Wo, Ho, corners);
         score[br] = h[best];
         gap[br] = (P > 1) ? h[best] - second : INFINITY;
     }

@@ -17,8 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
-GKD_ABI_VERSION = 3          # include/gkdhead.h
+GKD_ABI_VERSION = 4          # include/gkdhead.h
 GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
+GKD_COORDS_CORNERS = 0x4     # decode flag: corner-aligned -1..1 coordinates
 STATUS = {0: "GKD_OK", 1: "GKD_ERR_NULL", 2: "GKD_ERR_SHAPE", 3: "GKD_ERR_DTYPE",
           4: "GKD_ERR_VALUE", 5: "GKD_ERR_UNSUPPORTED", 6: "GKD_ERR_HIP",
           7: "GKD_ERR_ALIGN"}
@@ -127,7 +128,8 @@ def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
 
 def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=None,
                    mask_txt=None, decode: bool = True, out=None, out_decode=None,
-                   heat_dtype=torch.float32, with_heatmaps: bool = True):
+                   heat_dtype=torch.float32, with_heatmaps: bool = True,
+                   coords: str = "centres"):
     """query [B,C,H,W] (f32|bf16); kern_* [B,R,C] in the query dtype with
     mask_* [B,R] u8 (None = modality absent).
 
@@ -155,7 +157,7 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
         raise ValueError("at least one prompt modality is required")
     if heat_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"heat_dtype must be float32 or bfloat16, got {heat_dtype}")
-    flags = GKD_HEATMAP_BF16 if heat_dtype == torch.bfloat16 else 0
+    flags = (GKD_HEATMAP_BF16 if heat_dtype == torch.bfloat16 else 0) | _coords_flag(coords)
     if not with_heatmaps:
         if not decode:
             raise ValueError("with_heatmaps=False needs decode=True")
@@ -186,9 +188,17 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
     return out
 
 
-def peak_decode(heat: torch.Tensor, row_valid: torch.Tensor | None = None):
+def _coords_flag(coords: str) -> int:
+    if coords not in ("centres", "corners"):
+        raise ValueError("coords must be 'centres' or 'corners'")
+    return GKD_COORDS_CORNERS if coords == "corners" else 0
+
+
+def peak_decode(heat: torch.Tensor, row_valid: torch.Tensor | None = None,
+                coords: str = "centres"):
     """heat [B,R,Ho,Wo] f32, row_valid [B,R] u8 or None -> (idx [B,R] i32,
-    xy [B,R,2] f32, score [B,R] f32); invalid rows get (-1, NaN, -inf)."""
+    xy [B,R,2] f32, score [B,R] f32); invalid rows get (-1, NaN, -inf).
+    coords: "centres" ((2x + 1)/Wo - 1) or "corners" (2x/(Wo - 1) - 1)."""
     lib = load()
     _dev(heat, "heat", torch.float32, 4)
     B, R, Ho, Wo = heat.shape
@@ -199,8 +209,8 @@ def peak_decode(heat: torch.Tensor, row_valid: torch.Tensor | None = None):
     idx = torch.empty((B, R), dtype=torch.int32, device=heat.device)
     xy = torch.empty((B, R, 2), dtype=torch.float32, device=heat.device)
     score = torch.empty((B, R), dtype=torch.float32, device=heat.device)
-    _check(lib.gkd_peak_decode(_ptr(heat), _ptr(row_valid), B, R, Ho, Wo, 0, _ptr(idx),
-                               _ptr(xy), _ptr(score), _stream(heat.device)))
+    _check(lib.gkd_peak_decode(_ptr(heat), _ptr(row_valid), B, R, Ho, Wo, _coords_flag(coords),
+                               _ptr(idx), _ptr(xy), _ptr(score), _stream(heat.device)))
     return idx, xy, score
 
 

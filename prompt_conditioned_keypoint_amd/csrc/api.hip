@@ -101,7 +101,7 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
                               int H, int W, int R, gkd_dtype dtype, uint32_t flags,
                               void* heatmaps, int32_t* peak_idx, float* peak_xy,
                               float* peak_score, hipStream_t stream) {
-  if ((flags & ~(uint32_t)GKD_HEATMAP_BF16) != 0)
+  if ((flags & ~(uint32_t)(GKD_HEATMAP_BF16 | GKD_COORDS_CORNERS)) != 0)
     return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: unknown flags 0x%x", (unsigned)flags);
   if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
     return fail(GKD_ERR_DTYPE, "gkd_kernel_heatmap: unknown dtype %d", (int)dtype);
@@ -156,6 +156,7 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   a.bf16 = dtype == GKD_DTYPE_BF16;
   a.heat = heatmaps;
   a.heat_bf16 = (flags & GKD_HEATMAP_BF16) != 0;
+  a.corners = (flags & GKD_COORDS_CORNERS) != 0;
   a.idx = peak_idx;
   a.xy = peak_xy;
   a.score = peak_score;
@@ -165,7 +166,8 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
 gkd_status gkd_peak_decode(const float* heatmaps, const uint8_t* row_valid, int B, int R, int Ho,
                            int Wo, uint32_t flags, int32_t* peak_idx, float* peak_xy,
                            float* peak_score, hipStream_t stream) {
-  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_peak_decode: flags must be 0");
+  if ((flags & ~(uint32_t)GKD_COORDS_CORNERS) != 0)
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_peak_decode: unknown flags 0x%x", (unsigned)flags);
   if (B < 0 || R < 0 || Ho < 1 || Wo < 1)
     return fail(GKD_ERR_SHAPE, "gkd_peak_decode: bad shape B=%d R=%d Ho=%d Wo=%d", B, R, Ho, Wo);
   if ((long long)B * R * Ho * Wo > kMaxElems || (long long)B * R * 2 > kMaxElems)
@@ -185,6 +187,7 @@ gkd_status gkd_peak_decode(const float* heatmaps, const uint8_t* row_valid, int 
   a.idx = peak_idx;
   a.xy = peak_xy;
   a.score = peak_score;
+  a.corners = (flags & GKD_COORDS_CORNERS) != 0;
   return hip_status(gkd::launch_decode(a, stream), "gkd_peak_decode");
 }
 

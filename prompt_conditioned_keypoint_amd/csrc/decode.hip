@@ -71,8 +71,8 @@ __global__ __launch_bounds__(kDThreads) void decode_kernel(DecodeArgs p) {
       }
     const int y = bi / p.Wo, x = bi - y * p.Wo;
     p.idx[row] = bi;
-    p.xy[2 * row] = (float)(2 * x + 1) / (float)p.Wo - 1.f;
-    p.xy[2 * row + 1] = (float)(2 * y + 1) / (float)p.Ho - 1.f;
+    p.xy[2 * row] = keypoint_coord(x, p.Wo, p.corners);
+    p.xy[2 * row + 1] = keypoint_coord(y, p.Ho, p.corners);
     p.score[row] = bv;
   }
 }

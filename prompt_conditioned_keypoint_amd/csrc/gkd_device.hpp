@@ -29,6 +29,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
 
+// The -1..1 coordinate of index x of n along one axis: the cell centre
+// (2x + 1)/n - 1, or with corners the corner-aligned 2x/(n - 1) - 1 (0 for
+// n == 1).
+__device__ __forceinline__ float keypoint_coord(int x, int n, bool corners) {
+  if (!corners) return (float)(2 * x + 1) / (float)n - 1.f;
+  return n > 1 ? (float)(2 * x) / (float)(n - 1) - 1.f : 0.f;
+}
+
 // Argmax order: larger value first, then the lower flat index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);

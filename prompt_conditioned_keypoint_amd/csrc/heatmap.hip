@@ -59,6 +59,7 @@ struct HmParams {
   int32_t* idx;
   float* xy;
   float* score;
+  bool corners;    // corner-aligned keypoint coordinates
 };
 
 // ---------------------------------------------------------------------------
@@ -432,8 +433,8 @@ void heatmap_kernel(HmParams p) {
     const size_t o = (size_t)b * p.R + s_rows[tid];
     const int y = bi / Wo, x = bi - y * Wo;
     p.idx[o] = bi;
-    p.xy[2 * o] = (float)(2 * x + 1) / (float)Wo - 1.f;
-    p.xy[2 * o + 1] = (float)(2 * y + 1) / (float)Ho - 1.f;
+    p.xy[2 * o] = keypoint_coord(x, Wo, p.corners);
+    p.xy[2 * o + 1] = keypoint_coord(y, Ho, p.corners);
     p.score[o] = bv;
   }
 }
@@ -483,6 +484,7 @@ hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream) {
   p.heat = a.heat;
   p.heat_bf16 = a.heat_bf16;
   p.idx = a.idx;
+  p.corners = a.corners;
   p.xy = a.xy;
   p.score = a.score;
 

@@ -265,14 +265,14 @@ __device__ __forceinline__ void row_peak(const float* P, int* hl, const RowGeom&
   best_i = bi;
 }
 
-// keypoint record of one row: flat index, cell-centre -1..1 coordinates,
-// raw score
+// keypoint record of one row: flat index, -1..1 coordinates (cell centres
+// or corner-aligned), raw score
 __device__ __forceinline__ void write_keypoint(int32_t* idx, float* xy, float* score, size_t o,
-                                               float bv, int bi, int Ho, int Wo) {
+                                               float bv, int bi, int Ho, int Wo, bool corners) {
   const int y = bi / Wo, x = bi - y * Wo;
   idx[o] = bi;
-  xy[2 * o] = (float)(2 * x + 1) / (float)Wo - 1.f;
-  xy[2 * o + 1] = (float)(2 * y + 1) / (float)Ho - 1.f;
+  xy[2 * o] = keypoint_coord(x, Wo, corners);
+  xy[2 * o + 1] = keypoint_coord(y, Ho, corners);
   score[o] = bv;
 }
 
@@ -337,6 +337,7 @@ struct ContractParams {
   int32_t* idx;
   float* xy;
   float* score;
+  bool corners;          // corner-aligned keypoint coordinates
   uint64_t magic_w;      // ceil(2^32 / W)
 };
 
@@ -691,7 +692,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
           row_peak<false>(Pl + (size_t)r * pitch, hl, g, lane, bv, bi);
         if (lane == 0)
           write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + s_rows[base + r], bv, bi, g.Ho,
-                         g.Wo);
+                         g.Wo, p.corners);
       }
       lds_barrier();
     }
@@ -1085,6 +1086,7 @@ struct ExpandParams {
   int32_t* idx;
   float* xy;
   float* score;
+  bool corners;          // corner-aligned keypoint coordinates
 };
 
 // One wave per valid row of the crop (by rank).
@@ -1141,7 +1143,8 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   float bv;
   int bi;
   expand_row<SMALLW, BF16 ? kOutBf16 : kOutF32>(P, out, g, lane, p.idx != nullptr, bv, bi);
-  if (p.idx && lane == 0) write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + row, bv, bi, p.Ho, p.Wo);
+  if (p.idx && lane == 0) write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + row, bv, bi, p.Ho, p.Wo,
+                                     p.corners);
 }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -1260,6 +1263,7 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.idx = a.idx;
   cp.xy = a.xy;
   cp.score = a.score;
+  cp.corners = a.corners;
   cp.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
   const long long cgrid = crops_pad * cp.items_per_crop;
   if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;
@@ -1284,6 +1288,7 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   ep.heat = heat;
   ep.row_f = row_f;
   ep.idx = a.idx;
+  ep.corners = a.corners;
   ep.xy = a.xy;
   ep.score = a.score;
   const long long egrid = crops_pad * ep.groups_per_crop;

@@ -20,6 +20,7 @@ struct HeatmapArgs {
   int32_t* idx;
   float* xy;
   float* score;
+  bool corners;    // decode: corner-aligned -1..1 coordinates
 };
 
 struct VkpArgs {
@@ -39,6 +40,7 @@ struct DecodeArgs {
   int32_t* idx;
   float* xy;
   float* score;
+  bool corners;    // corner-aligned -1..1 coordinates
 };
 
 struct RoiArgs {

@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 3
+    assert lib.gkd_abi_version() == 4
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",

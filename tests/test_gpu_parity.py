@@ -571,3 +571,56 @@ def test_planted_peaks_recovered_at_high_snr(gkd):
             i, j = divmod(int(cells[b, r]), W)
             y, x = divmod(int(idx[b, r]), 4 * W)
             assert y in (4 * i + 1, 4 * i + 2) and x in (4 * j + 1, 4 * j + 2)
+
+
+def _corner_xy(idx, Ho, Wo):
+    x, y = idx % Wo, idx // Wo
+    return np.stack([2.0 * x / (Wo - 1) - 1.0, 2.0 * y / (Ho - 1) - 1.0], axis=-1)
+
+
+def test_corner_coordinates(gkd, ora):
+    """GKD_COORDS_CORNERS: the standalone decode matches the oracle's corner
+    convention (same index, coordinates within two float32 roundings); the
+    fused decode of the streamed, general and keypoints-only paths returns
+    the same indices and scores as with cell centres and the corner-aligned
+    coordinates of those indices."""
+    rng = np.random.default_rng(17)
+    h = rng.standard_normal((3, 7, 40, 24)).astype(np.float32)
+    valid = (rng.random((3, 7)) < 0.7).astype(np.uint8)
+    print("[corners] standalone decode", flush=True)
+    idx, xy, score = gkd.peak_decode(dev_tensor(h), dev_tensor(valid), coords="corners")
+    torch.cuda.synchronize()
+    o_idx, o_xy, o_score, _ = ora.peak_decode(h.astype(np.float64), valid, corners=True)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    ok = valid > 0
+    assert np.abs(xy.cpu().numpy()[ok] - o_xy[ok]).max() <= 2.0 ** -23
+    assert np.all(np.isnan(xy.cpu().numpy()[~ok]))
+    d = workload("longtail_bf16")
+    q = dev_tensor(d["query"], torch.bfloat16)
+    kv = dev_tensor(np.nan_to_num(gkdsynth.round_bf16_f32(np.random.default_rng(3).standard_normal(
+        (d["B"], d["R"], d["C"])).astype(np.float32))), torch.bfloat16)
+    mv, mt = dev_tensor(d["mask_vis"]), dev_tensor(d["mask_txt"])
+    kt = dev_tensor(np.nan_to_num(d["kern_txt"]), torch.bfloat16)
+    Ho, Wo = 4 * d["H"], 4 * d["W"]
+    valid = (d["mask_vis"] | d["mask_txt"]) > 0
+    for kw in ({}, {"with_heatmaps": False}):
+        print(f"[corners] fused {kw}", flush=True)
+        a = gkd.kernel_heatmap(q, kv, mv, kt, mt, **kw)
+        c = gkd.kernel_heatmap(q, kv, mv, kt, mt, coords="corners", **kw)
+        torch.cuda.synchronize()
+        (ia, _, sa), (ic, xc, sc) = (a if kw else a[1]), (c if kw else c[1])
+        assert torch.equal(ia, ic) and torch.equal(sa.view(torch.int32), sc.view(torch.int32))
+        want = _corner_xy(ic.cpu().numpy(), Ho, Wo)
+        assert np.abs(xc.cpu().numpy()[valid] - want[valid]).max() <= 2.0 ** -23
+    # the general kernel (float32 features)
+    rng = np.random.default_rng(23)
+    qf = rng.standard_normal((2, 64, 8, 8)).astype(np.float32)
+    kf = rng.standard_normal((2, 5, 64)).astype(np.float32)
+    m = np.ones((2, 5), np.uint8)
+    print("[corners] general kernel", flush=True)
+    _, (ia, _, _) = gkd.kernel_heatmap(dev_tensor(qf), dev_tensor(kf), dev_tensor(m))
+    _, (ic, xc, _) = gkd.kernel_heatmap(dev_tensor(qf), dev_tensor(kf), dev_tensor(m),
+                                        coords="corners")
+    torch.cuda.synchronize()
+    assert torch.equal(ia, ic)
+    assert np.abs(xc.cpu().numpy() - _corner_xy(ic.cpu().numpy(), 32, 32)).max() <= 2.0 ** -23

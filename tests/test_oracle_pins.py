@@ -281,6 +281,26 @@ def test_decode_matches_numpy_argmax_and_partition(oracle_mod):
     assert abs(xy3[0, 0, 1] - (-1 + 1 / Ho)) < 1e-15
 
 
+@pytest.mark.parametrize("Ho,Wo", [(96, 96), (7, 5), (1, 4), (3, 1)])
+def test_decode_corner_coordinates_are_linspace(oracle_mod, Ho, Wo):
+    """Corner-aligned coordinates: index i of n sits at numpy's
+    linspace(-1, 1, n)[i] (0 for a one-cell axis); the default cell-centre
+    coordinates are the midpoints of n equal cells of [-1, 1]. Every cell is
+    made the peak once."""
+    P = Ho * Wo
+    heat = np.zeros((1, P, Ho, Wo))
+    heat.reshape(P, P)[np.arange(P), np.arange(P)] = 1.0
+    idx, xy, _, _ = oracle_mod.peak_decode(heat, corners=True)
+    _, xyc, _, _ = oracle_mod.peak_decode(heat)
+    lx = np.linspace(-1, 1, Wo) if Wo > 1 else np.zeros(1)
+    ly = np.linspace(-1, 1, Ho) if Ho > 1 else np.zeros(1)
+    np.testing.assert_array_equal(idx[0], np.arange(P))
+    np.testing.assert_allclose(xy[0, :, 0], lx[np.arange(P) % Wo], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(xy[0, :, 1], ly[np.arange(P) // Wo], rtol=0, atol=1e-15)
+    mid_x = (np.linspace(-1, 1, Wo + 1)[:-1] + np.linspace(-1, 1, Wo + 1)[1:]) / 2
+    np.testing.assert_allclose(xyc[0, :, 0], mid_x[np.arange(P) % Wo], rtol=0, atol=1e-15)
+
+
 def test_decode_sentinel_rows(oracle_mod):
     h = np.random.default_rng(9).standard_normal((2, 3, 4, 4))
     valid = np.array([[1, 0, 1], [0, 0, 1]], np.uint8)
