@@ -58,10 +58,10 @@ def _load():
         lib.gko_vkp_pool.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _D, _D,
                                      _I, _P]
         lib.gko_upsample4.restype = _I
-        lib.gko_upsample4.argtypes = [_P, _I, _I, _I, _P]
+        lib.gko_upsample4.argtypes = [_P, _I, _I, _I, _I, _P]
         lib.gko_kernel_heatmap.restype = _I
         lib.gko_kernel_heatmap.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I,
-                                           _I, _I, _P]
+                                           _I, _I, _I, _P]
         lib.gko_roi_preprocess.restype = _I
         lib.gko_roi_preprocess.argtypes = [_P, _I, _I, _P, _I, _I, _P]
         lib.gko_roi_backproject.restype = _I
@@ -127,20 +127,22 @@ def vkp_pool(support, kpts, valid, stride=16.0, sigma=14.0, dtype="f64"):
     return out
 
 
-def upsample4(F):
-    """F [C,H,W] -> G [C,4H,4W] (half-pixel bilinear, edge clamp)."""
+def upsample4(F, corners=False):
+    """F [C,H,W] -> G [C,4H,4W] (half-pixel bilinear, edge clamp; with
+    corners the align_corners=True grid)."""
     lib = _load()
     f = _f64(F)
     C, H, W = f.shape
     G = np.empty((C, 4 * H, 4 * W))
-    _check(lib.gko_upsample4(_ptr(f), C, H, W, _ptr(G)), "upsample4")
+    _check(lib.gko_upsample4(_ptr(f), C, H, W, 1 if corners else 0, _ptr(G)), "upsample4")
     return G
 
 
 def kernel_heatmap(query, kern_vis=None, mask_vis=None, kern_txt=None,
-                   mask_txt=None):
+                   mask_txt=None, corners=False):
     """query [B,C,H,W]; kernels [B,R,C] + masks [B,R] per modality (None =
-    modality absent) -> heatmaps [B,R,4H,4W], NaN where no mask is set."""
+    modality absent) -> heatmaps [B,R,4H,4W], NaN where no mask is set.
+    corners: upsample on the align_corners=True grid."""
     lib = _load()
     q = _f64(query)
     B, C, H, W = q.shape
@@ -153,7 +155,7 @@ def kernel_heatmap(query, kern_vis=None, mask_vis=None, kern_txt=None,
     out = np.full((B, R, 4 * H, 4 * W), np.nan)
     _check(lib.gko_kernel_heatmap(_ptr(q), _ptr(kv), _ptr(_u8(mask_vis)),
                                   _ptr(kt), _ptr(_u8(mask_txt)), B, C, H, W,
-                                  R, _ptr(out)), "kernel_heatmap")
+                                  R, 1 if corners else 0, _ptr(out)), "kernel_heatmap")
     return out
 
 

@@ -136,7 +136,9 @@ int gko_vkp_pool(const double *support, const double *kpts,
 }
 
 /* ---------------------------------------------------------------------- */
-/* 4x bilinear upsample, half-pixel centres, edge clamp.                   */
+/* 4x bilinear upsample, half-pixel centres, edge clamp; or with corners   */
+/* the align_corners=True grid, whose first and last samples sit on the    */
+/* first and last source samples: source position out (n - 1)/(4n - 1).   */
 /* ---------------------------------------------------------------------- */
 typedef struct {
     int n;       /* 1 or 2 taps */
@@ -144,9 +146,13 @@ typedef struct {
     double a[2];
 } taps_t;
 
-static taps_t up_taps(int out, int n_in)
+static taps_t up_taps(int out, int n_in, int corners)
 {
-    double src = ((double)out + 0.5) / GKO_UP - 0.5;
+    double src;
+    if (corners)
+        src = n_in > 1 ? (double)out * (n_in - 1) / (GKO_UP * n_in - 1.0) : 0.0;
+    else
+        src = ((double)out + 0.5) / GKO_UP - 0.5;
     if (src < 0.0) src = 0.0;
     const int i0 = (int)floor(src);
     const int i1 = (i0 + 1 < n_in) ? i0 + 1 : n_in - 1;
@@ -167,9 +173,9 @@ static taps_t up_taps(int out, int n_in)
 }
 
 /* One upsampled value G[c, y, x] of the map f = F[c] (H x W). */
-static double up_value(const double *f, int H, int W, int y, int x)
+static double up_value(const double *f, int H, int W, int y, int x, int corners)
 {
-    const taps_t ty = up_taps(y, H), tx = up_taps(x, W);
+    const taps_t ty = up_taps(y, H, corners), tx = up_taps(x, W, corners);
     double g = 0.0;
     for (int a = 0; a < ty.n; ++a)
         for (int b = 0; b < tx.n; ++b)
@@ -178,7 +184,7 @@ static double up_value(const double *f, int H, int W, int y, int x)
 }
 
 /* F [C,H,W] -> G [C,4H,4W] */
-int gko_upsample4(const double *F, int C, int H, int W, double *G)
+int gko_upsample4(const double *F, int C, int H, int W, int corners, double *G)
 {
     if (C < 1 || H < 1 || W < 1) return 2;
     const int Ho = GKO_UP * H, Wo = GKO_UP * W;
@@ -186,7 +192,7 @@ int gko_upsample4(const double *F, int C, int H, int W, double *G)
         for (int y = 0; y < Ho; ++y)
             for (int x = 0; x < Wo; ++x)
                 G[((long)c * Ho + y) * Wo + x] =
-                    up_value(F + (long)c * H * W, H, W, y, x);
+                    up_value(F + (long)c * H * W, H, W, y, x, corners);
     return 0;
 }
 
@@ -208,7 +214,7 @@ static void l2_normalise(const double *k, int C, double *out)
 int gko_kernel_heatmap(const double *query, const double *kern_vis,
                        const uint8_t *mask_vis, const double *kern_txt,
                        const uint8_t *mask_txt, int B, int C, int H, int W,
-                       int R, double *heat)
+                       int R, int corners, double *heat)
 {
     if (B < 0 || C < 1 || H < 1 || W < 1 || R < 0) return 2;
     const int Ho = GKO_UP * H, Wo = GKO_UP * W;
@@ -232,7 +238,7 @@ int gko_kernel_heatmap(const double *query, const double *kern_vis,
         for (long p = 0; p < P; ++p) {
             const int y = (int)(p / Wo), x = (int)(p % Wo);
             for (int c = 0; c < C; ++c)
-                G[p * C + c] = up_value(Fb + (long)c * H * W, H, W, y, x);
+                G[p * C + c] = up_value(Fb + (long)c * H * W, H, W, y, x, corners);
         }
 
         for (int r = 0; r < R; ++r) {

@@ -70,6 +70,37 @@ def test_upsample_close_to_torch_on_random(oracle_mod):
     np.testing.assert_allclose(G, ref, rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("H,W", [(5, 7), (1, 6), (6, 1), (24, 24)])
+def test_upsample_corners_matches_torch_interpolate(oracle_mod, H, W):
+    """The align_corners=True grid against torch's bilinear interpolate
+    with align_corners=True (float64), the corners exactly on the source
+    corners."""
+    rng = np.random.default_rng(H * 31 + W)
+    F = rng.standard_normal((3, H, W))
+    G = oracle_mod.upsample4(F, corners=True)
+    ref = torch.nn.functional.interpolate(torch.from_numpy(F)[None], scale_factor=4,
+                                          mode="bilinear", align_corners=True)[0].numpy()
+    np.testing.assert_allclose(G, ref, rtol=0, atol=1e-12)
+    assert np.array_equal(G[:, 0, 0], F[:, 0, 0]) and np.array_equal(G[:, -1, -1], F[:, -1, -1])
+
+
+def test_heatmap_corners_is_conv_of_corner_upsample(oracle_mod):
+    """With corners the heatmap is the normalised kernel applied to the
+    align_corners=True upsample (torch's), mask-averaged like the default."""
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((2, 8, 5, 6))
+    k = rng.standard_normal((2, 3, 8))
+    m = np.array([[1, 0, 1], [1, 1, 1]], np.uint8)
+    h = oracle_mod.kernel_heatmap(q, k, m, corners=True)
+    up = torch.nn.functional.interpolate(torch.from_numpy(q), scale_factor=4, mode="bilinear",
+                                         align_corners=True).numpy()
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    ref = np.einsum("brc,bcyx->bryx", kn, up)
+    ok = m > 0
+    np.testing.assert_allclose(h[ok], ref[ok], rtol=0, atol=1e-12)
+    assert np.all(np.isnan(h[~ok]))
+
+
 def test_upsample_constant_ramp_and_edge_duplicates(oracle_mod):
     F = np.full((1, 4, 5), 2.5)
     assert np.all(oracle_mod.upsample4(F) == 2.5)
