@@ -37,15 +37,15 @@
  *   - Every element count (e.g. B*R*4H*4W) must be below 2^31.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
  *   - `flags` must be 0 (else GKD_ERR_UNSUPPORTED), except for the
- *     heatmap output format flag of gkd_kernel_heatmap (GKD_HEATMAP_BF16)
- *     and the keypoint coordinate flag of gkd_kernel_heatmap and
- *     gkd_peak_decode (GKD_COORDS_CORNERS).
+ *     heatmap output format and upsample grid flags of gkd_kernel_heatmap
+ *     (GKD_HEATMAP_BF16, GKD_UPSAMPLE_CORNERS) and the keypoint coordinate
+ *     flag of gkd_kernel_heatmap and gkd_peak_decode (GKD_COORDS_CORNERS).
  *
  * ABI history: version 1 had float32 heatmaps only; version 2 adds
  * GKD_HEATMAP_BF16 (gkd_kernel_heatmap's heatmaps argument became void *,
  * which existing callers pass unchanged); version 3 adds the ROI stage
  * (gkd_roi_preprocess, gkd_roi_backproject); version 4 adds
- * GKD_COORDS_CORNERS.
+ * GKD_COORDS_CORNERS; version 5 adds GKD_UPSAMPLE_CORNERS.
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -57,11 +57,15 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 4
+#define GKD_ABI_VERSION 5
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
 #define GKD_HEATMAP_BF16 0x1u
+/* gkd_kernel_heatmap flag: upsample on the align_corners=True grid (first
+ * and last outputs on the first and last low-res samples: source position
+ * o (n - 1) / (4n - 1)) instead of half-pixel centres. */
+#define GKD_UPSAMPLE_CORNERS 0x2u
 /* gkd_kernel_heatmap and gkd_peak_decode flag: map the peak index to -1..1
  * corner-aligned, x = 2 col / (Wo - 1) - 1 (0 when Wo == 1), instead of
  * the cell centre (2 col + 1) / Wo - 1; likewise y. */
@@ -139,7 +143,8 @@ GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
  * generated kernels with the query features.
  *
  * For every (b, r) with mask_vis[b,r] or mask_txt[b,r] set (n = number of
- * set masks), with u = up4(query[b]) the half-pixel bilinear 4x upsample:
+ * set masks), with u = up4(query[b]) the half-pixel bilinear 4x upsample
+ * (or, with GKD_UPSAMPLE_CORNERS, the align_corners=True one):
  *   heatmaps[b,r,y,x] = (1/n) sum_{m set} sum_c k_m[b,r,c] u[c,y,x] / ||k_m[b,r]||
  * (||k|| is clamped below at 1e-12). Computed at low resolution and then
  * expanded, which is the same linear map. Rows with no mask set are not

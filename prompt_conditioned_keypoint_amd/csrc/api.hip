@@ -101,7 +101,7 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
                               int H, int W, int R, gkd_dtype dtype, uint32_t flags,
                               void* heatmaps, int32_t* peak_idx, float* peak_xy,
                               float* peak_score, hipStream_t stream) {
-  if ((flags & ~(uint32_t)(GKD_HEATMAP_BF16 | GKD_COORDS_CORNERS)) != 0)
+  if ((flags & ~(uint32_t)(GKD_HEATMAP_BF16 | GKD_UPSAMPLE_CORNERS | GKD_COORDS_CORNERS)) != 0)
     return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: unknown flags 0x%x", (unsigned)flags);
   if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
     return fail(GKD_ERR_DTYPE, "gkd_kernel_heatmap: unknown dtype %d", (int)dtype);
@@ -157,6 +157,7 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   a.heat = heatmaps;
   a.heat_bf16 = (flags & GKD_HEATMAP_BF16) != 0;
   a.corners = (flags & GKD_COORDS_CORNERS) != 0;
+  a.up_corners = (flags & GKD_UPSAMPLE_CORNERS) != 0;
   a.idx = peak_idx;
   a.xy = peak_xy;
   a.score = peak_score;

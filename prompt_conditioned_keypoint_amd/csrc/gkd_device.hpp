@@ -37,6 +37,21 @@ __device__ __forceinline__ float keypoint_coord(int x, int n, bool corners) {
   return n > 1 ? (float)(2 * x) / (float)(n - 1) - 1.f : 0.f;
 }
 
+// Taps of output o on the align_corners=True grid of a 4x upsample of n
+// samples: source position o (n - 1) / (4n - 1), from an exact integer
+// ratio (the upper tap clamps at the last sample; n == 1 has one).
+__device__ __forceinline__ void corner_taps(int o, int n, int& i0, int& i1, float& lam) {
+  if (n == 1) {
+    i0 = i1 = 0;
+    lam = 0.f;
+    return;
+  }
+  const int num = o * (n - 1), den = 4 * n - 1;
+  i0 = num / den;
+  lam = (float)(num - i0 * den) / (float)den;
+  i1 = i0 + 1 < n ? i0 + 1 : n - 1;
+}
+
 // Argmax order: larger value first, then the lower flat index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);

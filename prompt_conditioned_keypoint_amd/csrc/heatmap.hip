@@ -60,6 +60,7 @@ struct HmParams {
   float* xy;
   float* score;
   bool corners;    // corner-aligned keypoint coordinates
+  bool up_corners; // upsample on the align_corners=True grid
 };
 
 // ---------------------------------------------------------------------------
@@ -372,6 +373,45 @@ void heatmap_kernel(HmParams p) {
     const size_t out_e = ((size_t)b * p.R + s_rows[s]) * (size_t)Ho * Wo;  // row's first element
     float bv = -INFINITY;
     int bi = INT_MAX;
+    if (p.up_corners) {
+      // align_corners=True grid: thread takes 4-output chunks of the map
+      // in raster order (one output row, columns 4x .. 4x + 3)
+      for (int q = tid; q < Ho * p.W; q += kThreads) {
+        const int y = q / p.W, x4 = q - y * p.W;
+        int i0, i1;
+        float ly;
+        corner_taps(y, p.H, i0, i1, ly);
+        const float* p0 = Pr + (size_t)i0 * p.W;
+        const float* p1 = Pr + (size_t)i1 * p.W;
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int j0, j1;
+          float lx;
+          corner_taps(4 * x4 + e, p.W, j0, j1, lx);
+          const float top = fmaf(lx, p0[j1] - p0[j0], p0[j0]);
+          const float bot = fmaf(lx, p1[j1] - p1[j0], p1[j0]);
+          o[e] = fmaf(ly, bot - top, top);
+        }
+        const size_t e0 = out_e + 4 * (size_t)q;
+        if (p.heat == nullptr) {
+          // keypoints only: nothing is stored
+        } else if (p.heat_bf16) {
+          const u32x2 v = {
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[0], o[1]}, bf16x2)),
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[2], o[3]}, bf16x2))};
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.heat) + e0));
+        } else {
+          __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(static_cast<float*>(p.heat) + e0));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (better(o[e], 4 * q + e, bv, bi)) {
+            bv = o[e];
+            bi = 4 * q + e;
+          }
+      }
+    } else
     for (int cell = tid; cell < p.S; cell += kThreads) {
       const int i = cell / p.W, j = cell - i * p.W;
       const int im = i > 0 ? i - 1 : 0, ip = i < p.H - 1 ? i + 1 : i;
@@ -485,6 +525,7 @@ hipError_t launch_heatmap(const HeatmapArgs& a, hipStream_t stream) {
   p.heat_bf16 = a.heat_bf16;
   p.idx = a.idx;
   p.corners = a.corners;
+  p.up_corners = a.up_corners;
   p.xy = a.xy;
   p.score = a.score;
 

@@ -165,6 +165,58 @@ __device__ __forceinline__ void expand_row(const float* P, void* out_row, const 
   best_i = bi;
 }
 
+// One wave expands P (H x W in LDS) on the align_corners=True grid into
+// out ([4H][4W], OUT as for expand_row) in raster order: lane l takes the
+// 4-output chunks l, l + 64, ... of the map (one output row, columns
+// 4x .. 4x + 3), so a lane's outputs ascend in flat index and a strict >
+// keeps the first peak. Every output is the bilinear mix of the four
+// source samples around its position (corner_taps).
+template <int OUT>
+__device__ __forceinline__ void expand_row_corners(const float* P, void* out_row, const RowGeom& g,
+                                                   int lane, bool decode, float& best_v,
+                                                   int& best_i) {
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  const int nq = g.Ho * g.W;
+  for (int q = lane; q < nq; q += kWave) {
+    const int y = (int)(((uint64_t)(uint32_t)q * g.magic_w) >> 32), x4 = q - y * g.W;
+    int i0, i1;
+    float ly;
+    corner_taps(y, g.H, i0, i1, ly);
+    const float* p0 = P + i0 * g.W;
+    const float* p1 = P + i1 * g.W;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int j0, j1;
+      float lx;
+      corner_taps(4 * x4 + e, g.W, j0, j1, lx);
+      const float top = fmaf(lx, p0[j1] - p0[j0], p0[j0]);
+      const float bot = fmaf(lx, p1[j1] - p1[j0], p1[j0]);
+      o[e] = fmaf(ly, bot - top, top);
+    }
+    if constexpr (OUT == kOutBf16) {
+      const u32x2 v = {
+          __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[0], o[1]}, bf16x2)),
+          __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[2], o[3]}, bf16x2))};
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out_row)) + q);
+    } else if constexpr (OUT == kOutF32) {
+      __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]},
+                                  reinterpret_cast<f32x4*>(static_cast<float*>(out_row)) + q);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (o[e] > bv) {
+        bv = o[e];
+        bi = 4 * q + e;
+      }
+  }
+  if (!decode) return;
+  wave_argmax(bv, bi);
+  best_v = bv;
+  best_i = bi;
+}
+
 // Wave64 maximum (every lane gets it): the argmax lane pattern on values
 // alone.
 __device__ __forceinline__ float wave_max(float v) {
@@ -338,6 +390,7 @@ struct ContractParams {
   float* xy;
   float* score;
   bool corners;          // corner-aligned keypoint coordinates
+  bool up_corners;       // upsample on the align_corners=True grid
   uint64_t magic_w;      // ceil(2^32 / W)
 };
 
@@ -686,7 +739,9 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
       for (int r = wave; r < nrows; r += kCWaves) {
         float bv;
         int bi;
-        if (p.W <= kWave)
+        if (p.up_corners)
+          expand_row_corners<kOutNone>(Pl + (size_t)r * pitch, nullptr, g, lane, true, bv, bi);
+        else if (p.W <= kWave)
           row_peak<true>(Pl + (size_t)r * pitch, hl, g, lane, bv, bi);
         else
           row_peak<false>(Pl + (size_t)r * pitch, hl, g, lane, bv, bi);
@@ -1090,7 +1145,7 @@ struct ExpandParams {
 };
 
 // One wave per valid row of the crop (by rank).
-template <bool SMALLW, bool BF16>
+template <bool SMALLW, bool BF16, bool UPC>
 __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   extern __shared__ __align__(16) float lds_p[];
   const int lane = threadIdx.x & 63;
@@ -1142,7 +1197,10 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
   const RowGeom g{p.H, p.W, p.S, p.Ho, p.Wo, p.magic_w};
   float bv;
   int bi;
-  expand_row<SMALLW, BF16 ? kOutBf16 : kOutF32>(P, out, g, lane, p.idx != nullptr, bv, bi);
+  if constexpr (UPC)
+    expand_row_corners<BF16 ? kOutBf16 : kOutF32>(P, out, g, lane, p.idx != nullptr, bv, bi);
+  else
+    expand_row<SMALLW, BF16 ? kOutBf16 : kOutF32>(P, out, g, lane, p.idx != nullptr, bv, bi);
   if (p.idx && lane == 0) write_keypoint(p.idx, p.xy, p.score, (size_t)b * p.R + row, bv, bi, p.Ho, p.Wo,
                                      p.corners);
 }
@@ -1264,6 +1322,7 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.xy = a.xy;
   cp.score = a.score;
   cp.corners = a.corners;
+  cp.up_corners = a.up_corners;
   cp.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
   const long long cgrid = crops_pad * cp.items_per_crop;
   if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;
@@ -1293,15 +1352,18 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   ep.score = a.score;
   const long long egrid = crops_pad * ep.groups_per_crop;
   if (egrid > INT_MAX) return hipErrorInvalidConfiguration;
-#define GKD_EXPAND(SW, BF)                                                                   \
-  hipLaunchKernelGGL((expand_kernel<SW, BF>), dim3((unsigned)egrid), dim3(kEThreads),        \
+#define GKD_EXPAND(SW, BF, UPC)                                                              \
+  hipLaunchKernelGGL((expand_kernel<SW, BF, UPC>), dim3((unsigned)egrid), dim3(kEThreads),   \
                      sp.expand_lds, stream, ep)
-  if (a.W <= kWave) {
-    if (a.heat_bf16) GKD_EXPAND(true, true);
-    else GKD_EXPAND(true, false);
+  if (a.up_corners) {
+    if (a.heat_bf16) GKD_EXPAND(false, true, true);
+    else GKD_EXPAND(false, false, true);
+  } else if (a.W <= kWave) {
+    if (a.heat_bf16) GKD_EXPAND(true, true, false);
+    else GKD_EXPAND(true, false, false);
   } else {
-    if (a.heat_bf16) GKD_EXPAND(false, true);
-    else GKD_EXPAND(false, false);
+    if (a.heat_bf16) GKD_EXPAND(false, true, false);
+    else GKD_EXPAND(false, false, false);
   }
 #undef GKD_EXPAND
   return hipGetLastError();

@@ -21,6 +21,7 @@ struct HeatmapArgs {
   float* xy;
   float* score;
   bool corners;    // decode: corner-aligned -1..1 coordinates
+  bool up_corners; // upsample on the align_corners=True grid
 };
 
 struct VkpArgs {

@@ -624,3 +624,50 @@ def test_corner_coordinates(gkd, ora):
     torch.cuda.synchronize()
     assert torch.equal(ia, ic)
     assert np.abs(xc.cpu().numpy() - _corner_xy(ic.cpu().numpy(), 32, 32)).max() <= 2.0 ** -23
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 64, 8, 8, 16), (2, 256, 24, 24, 40), (1, 64, 32, 32, 6),
+                                   (3, 40, 5, 7, 9), (2, 32, 1, 8, 4), (3, 256, 4, 4, 12)])
+def test_align_corners_upsample(gkd, ora, dtype, shape):
+    """GKD_UPSAMPLE_CORNERS against the oracle's align_corners=True heatmaps
+    (streamed path with one and several pixel chunks, general kernel, a
+    one-row map, maps too small to park the combined kernels), the fused
+    decode, bfloat16 heatmaps (the float32 values rounded) and keypoints
+    only (the same keypoints, bit for bit, where the path is the same)."""
+    B, C, H, W, R = shape
+    rng = np.random.default_rng(3 * B + C + 7 * H + W + R)
+    q = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    kv = rng.standard_normal((B, R, C)).astype(np.float32)
+    kt = rng.standard_normal((B, R, C)).astype(np.float32)
+    mv = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mt = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mv[0, 0] = mt[0, 0] = 1
+    if B > 1:
+        mv[1] = mt[1] = 0
+    if dtype == "bf16":
+        q, kv, kt = (gkdsynth.round_bf16_f32(a) for a in (q, kv, kt))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    print(f"[corners-up] {dtype} {shape}", flush=True)
+    args = (dev_tensor(q, dt), dev_tensor(kv, dt), dev_tensor(mv), dev_tensor(kt, dt),
+            dev_tensor(mt))
+    out = sentinel((B, R, 4 * H, 4 * W))
+    heat, (idx, xy, score) = gkd.kernel_heatmap(*args, out=out, align_corners=True)
+    out16 = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.bfloat16, device="cuda")
+    h16, _ = gkd.kernel_heatmap(*args, out=out16, heat_dtype=torch.bfloat16, align_corners=True)
+    kp = gkd.kernel_heatmap(*args, with_heatmaps=False, align_corners=True)
+    torch.cuda.synchronize()
+    oh = ora.kernel_heatmap(q, kv, mv, kt, mt, corners=True)
+    valid = ((mv | mt) > 0).astype(np.uint8)
+    fl = floors_of(q)
+    check_heatmaps(heat.cpu().numpy(), oh, valid, dtype, fl)
+    check_decode((idx.cpu().numpy(), xy.cpu().numpy(), score.cpu().numpy()), oh, valid, dtype,
+                 floors=fl)
+    assert np.all(heat.view(torch.int32).cpu().numpy()[valid == 0] == NAN_BITS)
+    v = torch.from_numpy(valid > 0).cuda()
+    assert torch.equal(h16.view(torch.int16)[v], heat.to(torch.bfloat16).view(torch.int16)[v])
+    check_decode(tuple(t.cpu().numpy() for t in kp), oh, valid, dtype, floors=fl)
+    same_path = not (dtype == "bf16" and C % 32 == 0 and (H * W) % 16 == 0 and H * W > 576)
+    if same_path:
+        for g, f in zip(kp, (idx, xy, score)):
+            assert torch.equal(g.view(torch.int32), f.view(torch.int32))
