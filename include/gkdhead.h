@@ -37,15 +37,17 @@
  *   - Every element count (e.g. B*R*4H*4W) must be below 2^31.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
  *   - `flags` must be 0 (else GKD_ERR_UNSUPPORTED), except for the
- *     heatmap output format and upsample grid flags of gkd_kernel_heatmap
- *     (GKD_HEATMAP_BF16, GKD_UPSAMPLE_CORNERS) and the keypoint coordinate
+ *     heatmap output format, upsample grid and query layout flags of
+ *     gkd_kernel_heatmap (GKD_HEATMAP_BF16, GKD_UPSAMPLE_CORNERS,
+ *     GKD_QUERY_TOKENS with GKD_QUERY_SKIP) and the keypoint coordinate
  *     flag of gkd_kernel_heatmap and gkd_peak_decode (GKD_COORDS_CORNERS).
  *
  * ABI history: version 1 had float32 heatmaps only; version 2 adds
  * GKD_HEATMAP_BF16 (gkd_kernel_heatmap's heatmaps argument became void *,
  * which existing callers pass unchanged); version 3 adds the ROI stage
  * (gkd_roi_preprocess, gkd_roi_backproject); version 4 adds
- * GKD_COORDS_CORNERS; version 5 adds GKD_UPSAMPLE_CORNERS.
+ * GKD_COORDS_CORNERS; version 5 adds GKD_UPSAMPLE_CORNERS; version 6 adds
+ * GKD_QUERY_TOKENS.
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 5
+#define GKD_ABI_VERSION 6
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
@@ -70,6 +72,15 @@ extern "C" {
  * corner-aligned, x = 2 col / (Wo - 1) - 1 (0 when Wo == 1), instead of
  * the cell centre (2 col + 1) / Wo - 1; likewise y. */
 #define GKD_COORDS_CORNERS 0x4u
+/* gkd_kernel_heatmap flag: the query arrives as the ViT's token sequence,
+ * [B, skip + H*W, C] with channels last, pixel (y, x) at token
+ * skip + y*W + x; skip (the leading class / storage tokens, 0..255) goes in
+ * bits 8..15 via GKD_QUERY_SKIP. Needs bfloat16 features, C % 32 == 0 and
+ * H*W % 16 == 0 (H*W <= 576 for keypoints only), else
+ * GKD_ERR_UNSUPPORTED. The results equal, bit for bit, those of the same
+ * call on the [B, C, H, W] layout. */
+#define GKD_QUERY_TOKENS 0x8u
+#define GKD_QUERY_SKIP(n) (((uint32_t)(n) & 255u) << 8)
 
 #ifndef GKD_API
 #define GKD_API __attribute__((visibility("default")))
@@ -150,7 +161,8 @@ GKD_API gkd_status gkd_vkp_pool(const void *support, const float *kpts_px,
  * expanded, which is the same linear map. Rows with no mask set are not
  * written.
  *
- *   query      [B,C,H,W] dtype   query feature map
+ *   query      [B,C,H,W] dtype   query feature map (or, with GKD_QUERY_TOKENS,
+ *                                [B, skip + H*W, C] tokens)
  *   kern_vis   [B,R,C]   dtype   visual kernels; mask_vis [B,R] uint8.
  *                                Both NULL = no visual prompt in the batch.
  *   kern_txt   [B,R,C]   dtype   text kernels; mask_txt [B,R] uint8.

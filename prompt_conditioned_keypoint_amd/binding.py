@@ -17,10 +17,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
-GKD_ABI_VERSION = 5          # include/gkdhead.h
+GKD_ABI_VERSION = 6          # include/gkdhead.h
 GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
 GKD_UPSAMPLE_CORNERS = 0x2   # gkd_kernel_heatmap flag: align_corners=True upsample
 GKD_COORDS_CORNERS = 0x4     # decode flag: corner-aligned -1..1 coordinates
+GKD_QUERY_TOKENS = 0x8       # query as [B, skip + H*W, C] tokens; skip in bits 8..15
 STATUS = {0: "GKD_OK", 1: "GKD_ERR_NULL", 2: "GKD_ERR_SHAPE", 3: "GKD_ERR_DTYPE",
           4: "GKD_ERR_VALUE", 5: "GKD_ERR_UNSUPPORTED", 6: "GKD_ERR_HIP",
           7: "GKD_ERR_ALIGN"}
@@ -130,7 +131,8 @@ def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
 def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=None,
                    mask_txt=None, decode: bool = True, out=None, out_decode=None,
                    heat_dtype=torch.float32, with_heatmaps: bool = True,
-                   coords: str = "centres", align_corners: bool = False):
+                   coords: str = "centres", align_corners: bool = False,
+                   token_hw=None, token_skip: int = 0):
     """query [B,C,H,W] (f32|bf16); kern_* [B,R,C] in the query dtype with
     mask_* [B,R] u8 (None = modality absent).
 
@@ -141,10 +143,18 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
     (heatmaps NULL in the C call; decode must be True) and returns
     (idx, xy, score). coords: "centres" or "corners" (GKD_COORDS_CORNERS);
     align_corners: upsample on the align_corners=True grid
-    (GKD_UPSAMPLE_CORNERS)."""
+    (GKD_UPSAMPLE_CORNERS). token_hw=(H, W): the query is the ViT's token
+    sequence [B, token_skip + H*W, C] (GKD_QUERY_TOKENS)."""
     lib = load()
-    _dev(query, "query", ndim=4)
-    B, C, H, W = query.shape
+    if token_hw is None:
+        _dev(query, "query", ndim=4)
+        B, C, H, W = query.shape
+    else:
+        _dev(query, "query", ndim=3)
+        H, W = (int(v) for v in token_hw)
+        B, T, C = query.shape
+        if not 0 <= token_skip <= 255 or T != token_skip + H * W:
+            raise ValueError("query must be [B, token_skip + H*W, C] with 0 <= token_skip <= 255")
     R = None
     for k, m, name in ((kern_vis, mask_vis, "vis"), (kern_txt, mask_txt, "txt")):
         if (k is None) != (m is None):
@@ -161,7 +171,8 @@ def kernel_heatmap(query: torch.Tensor, kern_vis=None, mask_vis=None, kern_txt=N
     if heat_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"heat_dtype must be float32 or bfloat16, got {heat_dtype}")
     flags = ((GKD_HEATMAP_BF16 if heat_dtype == torch.bfloat16 else 0) | _coords_flag(coords) |
-             (GKD_UPSAMPLE_CORNERS if align_corners else 0))
+             (GKD_UPSAMPLE_CORNERS if align_corners else 0) |
+             (GKD_QUERY_TOKENS | (token_skip << 8) if token_hw is not None else 0))
     if not with_heatmaps:
         if not decode:
             raise ValueError("with_heatmaps=False needs decode=True")

@@ -101,14 +101,18 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
                               int H, int W, int R, gkd_dtype dtype, uint32_t flags,
                               void* heatmaps, int32_t* peak_idx, float* peak_xy,
                               float* peak_score, hipStream_t stream) {
-  if ((flags & ~(uint32_t)(GKD_HEATMAP_BF16 | GKD_UPSAMPLE_CORNERS | GKD_COORDS_CORNERS)) != 0)
+  constexpr uint32_t kKnown = GKD_HEATMAP_BF16 | GKD_UPSAMPLE_CORNERS | GKD_COORDS_CORNERS |
+                              GKD_QUERY_TOKENS | GKD_QUERY_SKIP(255);
+  const bool tokens = (flags & GKD_QUERY_TOKENS) != 0;
+  const int skip = (int)((flags >> 8) & 255u);
+  if ((flags & ~kKnown) != 0 || (!tokens && skip != 0))
     return fail(GKD_ERR_UNSUPPORTED, "gkd_kernel_heatmap: unknown flags 0x%x", (unsigned)flags);
   if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
     return fail(GKD_ERR_DTYPE, "gkd_kernel_heatmap: unknown dtype %d", (int)dtype);
   if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1)
     return fail(GKD_ERR_SHAPE, "gkd_kernel_heatmap: bad shape B=%d C=%d H=%d W=%d R=%d", B, C,
                 H, W, R);
-  if ((long long)B * C * H * W > kMaxElems || (long long)B * R * C > kMaxElems ||
+  if ((long long)B * C * ((long long)H * W + skip) > kMaxElems || (long long)B * R * C > kMaxElems ||
       (long long)B * R * 16 * H * W > kMaxElems || (long long)B * R * 2 > kMaxElems)
     return fail(GKD_ERR_SHAPE, "gkd_kernel_heatmap: an element count reaches 2^31");
   if ((long long)H * W > gkd::kHeatmapMaxS)
@@ -117,9 +121,13 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   {
     const bool bf16 = dtype == GKD_DTYPE_BF16;
     const bool kp = heatmaps == nullptr;
-    const bool fits = gkd::heatmap_stream_applicable(C, H * W, bf16, kp)
-                          ? gkd::plan_heatmap_stream(B, C, H * W, R, kp).ok
-                          : gkd::plan_heatmap(C, H * W, bf16).rows_per_item >= 1;
+    const bool stream = gkd::heatmap_stream_applicable(C, H * W, bf16, kp);
+    if (tokens && !stream)
+      return fail(GKD_ERR_UNSUPPORTED,
+                  "gkd_kernel_heatmap: token-layout queries need bfloat16 features, C %% 32 == 0 "
+                  "and H*W %% 16 == 0 (H*W <= 576 for keypoints only)");
+    const bool fits = stream ? gkd::plan_heatmap_stream(B, C, H * W, R, kp, tokens).ok
+                             : gkd::plan_heatmap(C, H * W, bf16).rows_per_item >= 1;
     if (!fits)
       return fail(GKD_ERR_UNSUPPORTED,
                   "gkd_kernel_heatmap: H*W=%d does not fit the kernel's LDS budget", H * W);
@@ -158,6 +166,8 @@ gkd_status gkd_kernel_heatmap(const void* query, const void* kern_vis, const uin
   a.heat_bf16 = (flags & GKD_HEATMAP_BF16) != 0;
   a.corners = (flags & GKD_COORDS_CORNERS) != 0;
   a.up_corners = (flags & GKD_UPSAMPLE_CORNERS) != 0;
+  a.tokens = tokens;
+  a.tok_skip = skip;
   a.idx = peak_idx;
   a.xy = peak_xy;
   a.score = peak_score;

@@ -391,6 +391,8 @@ struct ContractParams {
   float* score;
   bool corners;          // corner-aligned keypoint coordinates
   bool up_corners;       // upsample on the align_corners=True grid
+  int tok_T, tok_skip;   // query as tokens [B, tok_T, C], pixel s at token tok_skip + s
+                         //   (tok_T == 0: [B, C, H, W])
   uint64_t magic_w;      // ceil(2^32 / W)
 };
 
@@ -479,18 +481,24 @@ __device__ __forceinline__ uint64_t dma_source(const DmaPlan& pl, const DmaBases
 
 // cache policy of the feature loads: non-temporal (each feature byte is
 // read once, so the stream should not displace what the next passes reuse
-// from L2 and the memory-side cache)
+// from L2 and the memory-side cache). Token-layout loads keep the default
+// policy: a step reads half of each pixel's 128-byte line and the next
+// step the other half, which then comes from L2.
 constexpr int kFeatureCpol = 2;
 
 // feature blocks of one step into feature slot fs
 __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases& bs,
-                                               unsigned char* fs, int wave, int step) {
+                                               unsigned char* fs, int wave, int step, bool tok) {
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
-    if (i < pl.nf && ((pl.live >> i) & 1u))
-      __builtin_amdgcn_global_load_lds((glb_void*)dma_source(pl, bs, i, step),
-                                       (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024),
-                                       16, 0, kFeatureCpol);
+    if (i < pl.nf && ((pl.live >> i) & 1u)) {
+      glb_void* src = (glb_void*)dma_source(pl, bs, i, step);
+      lds_void* dst = (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024);
+      if (tok)
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kFeatureCpol);
+    }
 }
 
 // kernel-row blocks of two K steps (step, step + 1; step even) into
@@ -612,7 +620,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     // the loads of step k + ahead go to the slots step k - 1 used
     if (k + ahead < p.nsteps) {
       const int s = k + ahead;
-      issue_features(pl, bs, lds + (size_t)(s % kStages) * it.fbytes, wave, s);
+      issue_features(pl, bs, lds + (size_t)(s % kStages) * it.fbytes, wave, s, p.tok_T > 0);
       if ((s & 1) == 0)
         issue_rows(pl, bs, aring + (size_t)((s >> 1) % kPairSlots) * it.abytes, s, s + 1 == p.nsteps);
     }
@@ -645,29 +653,44 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
       }
     }
     // B: lane (n16, g4) of N tile t receives channels 8 g4 .. 8 g4 + 7 of
-    // pixel gpx + 16 t + n16 from two transposing 8-byte reads (rows
-    // 8 g4 + n16/4 and +4, columns 4 (n16 % 4) .. +3 of the tile)
-    const int r0 = 8 * g4 + (n16 >> 2);
-    const uint32_t lo_addr =
-        (uint32_t)(uintptr_t)(lds_void*)(sb + r0 * row_bytes + (gpx + 4 * (n16 & 3)) * 2);
-    const uint32_t hi_addr = lo_addr + 4 * row_bytes;
-    u32x2 blo[3], bhi[3];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %6\n"
-        "ds_read_b64_tr_b16 %1, %6 offset:32\n"
-        "ds_read_b64_tr_b16 %2, %6 offset:64\n"
-        "ds_read_b64_tr_b16 %3, %7\n"
-        "ds_read_b64_tr_b16 %4, %7 offset:32\n"
-        "ds_read_b64_tr_b16 %5, %7 offset:64\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(blo[0]), "=&v"(blo[1]), "=&v"(blo[2]), "=&v"(bhi[0]), "=&v"(bhi[1]),
-          "=&v"(bhi[2])
-        : "v"(lo_addr), "v"(hi_addr)
-        : "memory");
+    // pixel gpx + 16 t + n16. Tokens: 16 contiguous bytes of the pixel's
+    // slot (64 bytes a pixel); channel rows: two transposing 8-byte reads
+    // (rows 8 g4 + n16/4 and +4, columns 4 (n16 % 4) .. +3 of the tile)
+    u32x4 bw[3];
+    if (p.tok_T > 0) {
+      const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)(sb + (gpx + n16) * 64 + 16 * g4);
+      asm volatile(
+          "ds_read_b128 %0, %3\n"
+          "ds_read_b128 %1, %3 offset:1024\n"
+          "ds_read_b128 %2, %3 offset:2048\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(bw[0]), "=&v"(bw[1]), "=&v"(bw[2])
+          : "v"(addr)
+          : "memory");
+    } else {
+      const int r0 = 8 * g4 + (n16 >> 2);
+      const uint32_t lo_addr =
+          (uint32_t)(uintptr_t)(lds_void*)(sb + r0 * row_bytes + (gpx + 4 * (n16 & 3)) * 2);
+      const uint32_t hi_addr = lo_addr + 4 * row_bytes;
+      u32x2 blo[3], bhi[3];
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %6\n"
+          "ds_read_b64_tr_b16 %1, %6 offset:32\n"
+          "ds_read_b64_tr_b16 %2, %6 offset:64\n"
+          "ds_read_b64_tr_b16 %3, %7\n"
+          "ds_read_b64_tr_b16 %4, %7 offset:32\n"
+          "ds_read_b64_tr_b16 %5, %7 offset:64\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(blo[0]), "=&v"(blo[1]), "=&v"(blo[2]), "=&v"(bhi[0]), "=&v"(bhi[1]),
+            "=&v"(bhi[2])
+          : "v"(lo_addr), "v"(hi_addr)
+          : "memory");
+#pragma unroll
+      for (int t = 0; t < 3; ++t) bw[t] = u32x4{blo[t].x, blo[t].y, bhi[t].x, bhi[t].y};
+    }
     bf16x8 bv[3];
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
-      bv[t] = __builtin_bit_cast(bf16x8, u32x4{blo[t].x, blo[t].y, bhi[t].x, bhi[t].y});
+    for (int t = 0; t < 3; ++t) bv[t] = __builtin_bit_cast(bf16x8, bw[t]);
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
       const int h = h0 + u * hstep;
@@ -816,18 +839,21 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // set-up below from being hoisted and held across the K loop
   int lane_p = lane;
   asm volatile("" : "+v"(lane_p));
+  const bool tok = p.tok_T > 0;
   ItemShape it;
   it.ng = p.ng;
   it.chunk_px = it.ng * kGroupPx;
   it.rs = it.chunk_px / 8 + 1;
   it.px0 = chunk * p.chunk_px;
-  const int nF = kKS * it.rs;                   // feature slots of a step
+  // feature slots of a step: 32 channel rows of rs 16-byte columns, or with
+  // tokens 4 16-byte pieces (32 channels) per pixel, pixel-major
+  const int nF = tok ? 4 * it.chunk_px : kKS * it.rs;
   const int nfi = (nF + kWave - 1) / kWave;     // feature blocks
   it.fbytes = nfi * 1024;
 
   DmaBases bs;
-  bs.F = p.query + (size_t)b * p.C * p.S;
-  bs.fstep = (size_t)kKS * p.S;
+  bs.F = tok ? p.query + ((size_t)b * p.tok_T + p.tok_skip) * p.C : p.query + (size_t)b * p.C * p.S;
+  bs.fstep = tok ? (size_t)kKS : (size_t)kKS * p.S;
   bs.kv = bs.F;
   bs.kt = bs.F;
 
@@ -850,7 +876,15 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
     if (i >= pl.nf) continue;  // the kernel-row part sets its own bits below
     uint32_t kind = kSrcJunk, off = 0;
     const int u = (wave + kCWaves * i) * kWave + lane_p;
-    if (u < nF) {
+    if (u < nF && tok) {
+      // pixel px0 + u / 4, channels 8 (u % 4) .. + 7 of the step; past the
+      // map: junk (the pixels are never read)
+      const int px = it.px0 + (u >> 2);
+      if (px < p.S) {
+        kind = kSrcF;
+        off = (uint32_t)px * (uint32_t)p.C + 8u * (uint32_t)(u & 3);
+      }
+    } else if (u < nF) {
       const int r = u / it.rs, cc = u - r * it.rs;
       const int px = it.px0 + 8 * cc;
       if (cc < it.rs - 1) {
@@ -865,7 +899,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
       pl.live1 |= 1u << i;
     }
   }
-  issue_features(pl, bs, lds, wave, 0);
+  issue_features(pl, bs, lds, wave, 0, tok);
 
   if (wave == 0)
     select_rows(mv, mt, p.R, lane, rblk, kItemRows, s_rows, s_mv, s_mt, &s_nvalid, &s_nsel);
@@ -971,7 +1005,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // items of the batch a larger share of the memory bandwidth, so all
   // items finish closer together.
   it.ahead = it.arows <= p.light_arows ? 1 : kStages - 1;
-  if (it.ahead > 1 && p.nsteps > 1) issue_features(pl, bs, lds + (size_t)it.fbytes, wave, 1);
+  if (it.ahead > 1 && p.nsteps > 1) issue_features(pl, bs, lds + (size_t)it.fbytes, wave, 1, tok);
   unsigned char* const aring = lds + (size_t)kStages * it.fbytes;
   issue_rows(pl, bs, aring, 0, p.nsteps == 1);
 
@@ -1215,7 +1249,7 @@ bool heatmap_stream_applicable(int C, int S, bool bf16, bool keypoints_only) {
          (!keypoints_only || S <= kCWaves * kGroupPx);
 }
 
-StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps) {
+StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps, bool tokens) {
   StreamPlan sp;
   // wave groups per chunk: the fewest that still cover a small map in one
   // chunk, then fewer still while the batch leaves CUs idle (not when every
@@ -1235,7 +1269,7 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps) {
   int max_instr = 0;
   size_t max_lds = 0;
   auto need = [&](int chunk_px, int arows) {
-    const int nfi = ceil_div(kKS * (chunk_px / 8 + 1), kWave);
+    const int nfi = ceil_div(tokens ? 4 * chunk_px : kKS * (chunk_px / 8 + 1), kWave);
     const int nai = ceil_div(arows * kRowSlots, kWave);
     if (nfi + nai > max_instr) max_instr = nfi + nai;
     const size_t lds = (size_t)(kStages * nfi + kPairSlots * nai) * 1024;
@@ -1256,7 +1290,7 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps) {
 hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   const int S = a.H * a.W;
   const bool kp = a.heat == nullptr;  // keypoints only
-  const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R, kp);
+  const StreamPlan sp = plan_heatmap_stream(a.B, a.C, S, a.R, kp, a.tokens);
   if (!sp.ok) return hipErrorInvalidConfiguration;
   const long long crops_pad = (long long)(a.B + kXcds - 1) / kXcds * kXcds;
   float* const heat = static_cast<float*>(a.heat);
@@ -1322,6 +1356,8 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.xy = a.xy;
   cp.score = a.score;
   cp.corners = a.corners;
+  cp.tok_T = a.tokens ? a.tok_skip + S : 0;
+  cp.tok_skip = a.tokens ? a.tok_skip : 0;
   cp.up_corners = a.up_corners;
   cp.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
   const long long cgrid = crops_pad * cp.items_per_crop;

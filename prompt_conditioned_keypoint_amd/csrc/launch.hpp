@@ -22,6 +22,8 @@ struct HeatmapArgs {
   float* score;
   bool corners;    // decode: corner-aligned -1..1 coordinates
   bool up_corners; // upsample on the align_corners=True grid
+  int tok_skip;    // query as tokens [B, tok_skip + H*W, C] (channels last)
+  bool tokens;     //   when set; otherwise [B, C, H, W]
 };
 
 struct VkpArgs {
@@ -84,7 +86,7 @@ struct StreamPlan {
 // keypoints_only / whole_maps: no heatmaps are written and the decode runs
 // in the contraction, so every item must cover whole maps
 bool heatmap_stream_applicable(int C, int S, bool bf16, bool keypoints_only);
-StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps);
+StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps, bool tokens);
 hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream);
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

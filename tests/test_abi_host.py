@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 5
+    assert lib.gkd_abi_version() == 6
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
@@ -81,7 +81,11 @@ def dec(lib, heat=A, valid=None, B=2, R=80, Ho=96, Wo=96, flags=0, idx=A, xy=A2,
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(flags=8), UNSUP),              # only 0x1, 0x2 and 0x4 are defined
+    (dict(flags=0x10), UNSUP),           # only 0x1, 0x2, 0x4, 0x8 and the skip byte
+    (dict(flags=0x100), UNSUP),          # a token skip count without token layout
+    (dict(flags=0x8, dtype=0), UNSUP),   # token layout needs bfloat16 features
+    (dict(flags=0x8, dtype=1, C=40), UNSUP),        # ... and C % 32 == 0
+    (dict(flags=0x8, dtype=1, C=64, H=5, W=5), UNSUP),  # ... and H*W % 16 == 0
     (dict(flags=0x80000001), UNSUP),
     (dict(dtype=2), DTYPE),
     (dict(dtype=-1), DTYPE),
@@ -219,7 +223,7 @@ def test_roi_backproject_empty_is_ok(lib):
 
 def test_last_error_is_thread_local(lib):
     import threading
-    assert hm(lib, flags=8) == UNSUP
+    assert hm(lib, flags=0x10) == UNSUP
     seen = {}
 
     def other():

@@ -671,3 +671,76 @@ def test_align_corners_upsample(gkd, ora, dtype, shape):
     if same_path:
         for g, f in zip(kp, (idx, xy, score)):
             assert torch.equal(g.view(torch.int32), f.view(torch.int32))
+
+
+def _tokens(q, skip, rng):
+    """[B, C, H, W] -> the ViT's token sequence [B, skip + H*W, C] with
+    random leading tokens."""
+    B, C, H, W = q.shape
+    t = np.empty((B, skip + H * W, C), q.dtype)
+    t[:, :skip] = rng.standard_normal((B, skip, C)).astype(q.dtype) * 100
+    t[:, skip:] = q.reshape(B, C, H * W).transpose(0, 2, 1)
+    return np.ascontiguousarray(t)
+
+
+@pytest.mark.parametrize("skip", [0, 5])
+@pytest.mark.parametrize("shape", [(3, 64, 8, 8, 16), (2, 256, 24, 24, 40), (1, 64, 32, 32, 6),
+                                   (3, 256, 4, 4, 12), (2, 32, 6, 8, 200)])
+def test_query_tokens_layout(gkd, ora, shape, skip):
+    """GKD_QUERY_TOKENS: the token sequence [B, skip + H*W, C] gives, bit
+    for bit, the results of the same call on [B, C, H, W] (heatmaps,
+    bfloat16 heatmaps, the fused decode and keypoints only: the channel
+    order of every K step and the accumulation order are the same), and
+    the heatmaps match the oracle."""
+    B, C, H, W, R = shape
+    rng = np.random.default_rng(B + C + H + W + R + skip)
+    q = gkdsynth.round_bf16_f32(rng.standard_normal((B, C, H, W)).astype(np.float32))
+    kv = gkdsynth.round_bf16_f32(rng.standard_normal((B, R, C)).astype(np.float32))
+    kt = gkdsynth.round_bf16_f32(rng.standard_normal((B, R, C)).astype(np.float32))
+    mv = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mt = (rng.random((B, R)) < 0.5).astype(np.uint8)
+    mv[0, 0] = mt[0, 0] = 1
+    tok = dev_tensor(_tokens(q, skip, rng), torch.bfloat16)
+    bf = torch.bfloat16
+    rest = (dev_tensor(kv, bf), dev_tensor(mv), dev_tensor(kt, bf), dev_tensor(mt))
+    print(f"[tokens] {shape} skip={skip}", flush=True)
+    for kw in ({}, {"heat_dtype": bf}):
+        h0, d0 = gkd.kernel_heatmap(dev_tensor(q, bf), *rest, **kw)
+        h1, d1 = gkd.kernel_heatmap(tok, *rest, token_hw=(H, W), token_skip=skip, **kw)
+        torch.cuda.synchronize()
+        valid = torch.from_numpy((mv | mt) > 0).cuda()
+        iv = torch.int16 if kw else torch.int32
+        assert torch.equal(h0.view(iv)[valid], h1.view(iv)[valid])
+        for a, b in zip(d0, d1):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        if not kw:
+            oh = ora.kernel_heatmap(q, kv, mv, kt, mt)
+            check_heatmaps(h1.cpu().numpy(), oh, ((mv | mt) > 0).astype(np.uint8), "bf16",
+                           floors_of(q))
+    if H * W <= 576:
+        k0 = gkd.kernel_heatmap(dev_tensor(q, bf), *rest, with_heatmaps=False)
+        k1 = gkd.kernel_heatmap(tok, *rest, with_heatmaps=False, token_hw=(H, W), token_skip=skip)
+        torch.cuda.synchronize()
+        for a, b in zip(k0, k1):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_query_tokens_longtail(gkd):
+    """The long-tail batch with the query as tokens (5 leading tokens): the
+    same heatmaps and keypoints, bit for bit, as the [B, C, H, W] call."""
+    d = workload("longtail_bf16")
+    rng = np.random.default_rng(8)
+    q = dev_tensor(d["query"], torch.bfloat16)
+    tok = dev_tensor(_tokens(d["query"], 5, rng), torch.bfloat16)
+    kv = dev_tensor(np.nan_to_num(gkdsynth.round_bf16_f32(np.random.default_rng(3).standard_normal(
+        (d["B"], d["R"], d["C"])).astype(np.float32))), torch.bfloat16)
+    mv, mt = dev_tensor(d["mask_vis"]), dev_tensor(d["mask_txt"])
+    kt = dev_tensor(np.nan_to_num(d["kern_txt"]), torch.bfloat16)
+    print("[tokens] longtail", flush=True)
+    h0, d0 = gkd.kernel_heatmap(q, kv, mv, kt, mt)
+    h1, d1 = gkd.kernel_heatmap(tok, kv, mv, kt, mt, token_hw=(d["H"], d["W"]), token_skip=5)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy((d["mask_vis"] | d["mask_txt"]) > 0).cuda()
+    assert torch.equal(h0.view(torch.int32)[valid], h1.view(torch.int32)[valid])
+    for a, b in zip(d0, d1):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
