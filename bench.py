@@ -300,6 +300,33 @@ def dense_mode(torch, gkd, n=50):
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def tokens_mode(torch, gkd, d, kv, mv, kt, mt, heat, dec, heat_bytes, rows, n=50):
+    """The headline heatmap call with the query as the ViT's token sequence
+    [B, 5 + H*W, C] (class + storage tokens first; GKD_QUERY_TOKENS), timed
+    with events like the headline call; the results equal the headline's."""
+    B, C, H, W = d["B"], d["C"], d["H"], d["W"]
+    q = d["query"].reshape(B, C, H * W).transpose(0, 2, 1)
+    tok = np.concatenate([np.zeros((B, 5, C), np.float32), q], axis=1)
+    tok = torch.from_numpy(np.ascontiguousarray(tok)).to("cuda").to(torch.bfloat16)
+    call = lambda: gkd.kernel_heatmap(tok, kv, mv, kt, mt, out=heat, out_decode=dec,
+                                      token_hw=(H, W), token_skip=5)
+    for _ in range(5):
+        call()
+    evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        evs[k][0].record()
+        call()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gbs = heat_bytes / (ms * 1e-3) / 1e9
+    return {"note": "headline heatmap call with the query as [B, 5 + H*W, C] tokens "
+                    "(GKD_QUERY_TOKENS); not the headline",
+            "call_ms": round(ms, 4), "heatmaps_per_s_call": round(rows / (ms * 1e-3), 1),
+            "gbps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,7 +470,12 @@ def main():
         roi = roi_stage(torch, gkd, with_cpu=not args.no_cpu_baseline)
         log("[bench] dense long-tail batch")
         dense = dense_mode(torch, gkd)
+        log("[bench] token-layout query")
+        toks = tokens_mode(torch, gkd, d, protos if has_vis else None, mv if has_vis else None,
+                           kt if has_txt else None, mt if has_txt else None, heat,
+                           (idx, xy, score), heat_bytes, rows)
         modes = {
+            "query_tokens": toks,
             "longtail_dense": dense,
             "roi_stage": roi,
             "heatmap_bf16": {

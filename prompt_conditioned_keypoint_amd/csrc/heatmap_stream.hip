@@ -486,15 +486,16 @@ __device__ __forceinline__ uint64_t dma_source(const DmaPlan& pl, const DmaBases
 // step the other half, which then comes from L2.
 constexpr int kFeatureCpol = 2;
 
-// feature blocks of one step into feature slot fs
+// feature blocks of one step into feature slot fs (TOK: token layout)
+template <bool TOK>
 __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases& bs,
-                                               unsigned char* fs, int wave, int step, bool tok) {
+                                               unsigned char* fs, int wave, int step) {
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
     if (i < pl.nf && ((pl.live >> i) & 1u)) {
       glb_void* src = (glb_void*)dma_source(pl, bs, i, step);
       lds_void* dst = (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024);
-      if (tok)
+      if constexpr (TOK)
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       else
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kFeatureCpol);
@@ -554,7 +555,7 @@ struct ItemShape {
 // kPre (the same hi and lo parts, formed once by the row pass and staged
 // directly).
 // UPW: wave units (one M tile x one 48-pixel group) a wave may own.
-template <int MODE, int UPW>
+template <int MODE, int UPW, bool TOK>
 __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned char* lds,
                                               const DmaPlan& pl, const DmaBases& bs,
                                               const ItemShape& it, int b, int wave, int lane,
@@ -620,7 +621,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     // the loads of step k + ahead go to the slots step k - 1 used
     if (k + ahead < p.nsteps) {
       const int s = k + ahead;
-      issue_features(pl, bs, lds + (size_t)(s % kStages) * it.fbytes, wave, s, p.tok_T > 0);
+      issue_features<TOK>(pl, bs, lds + (size_t)(s % kStages) * it.fbytes, wave, s);
       if ((s & 1) == 0)
         issue_rows(pl, bs, aring + (size_t)((s >> 1) % kPairSlots) * it.abytes, s, s + 1 == p.nsteps);
     }
@@ -657,7 +658,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     // slot (64 bytes a pixel); channel rows: two transposing 8-byte reads
     // (rows 8 g4 + n16/4 and +4, columns 4 (n16 % 4) .. +3 of the tile)
     u32x4 bw[3];
-    if (p.tok_T > 0) {
+    if constexpr (TOK) {
       const uint32_t addr = (uint32_t)(uintptr_t)(lds_void*)(sb + (gpx + n16) * 64 + 16 * g4);
       asm volatile(
           "ds_read_b128 %0, %3\n"
@@ -799,7 +800,7 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
   }
 }
 
-template <int MODE, int MAXU>
+template <int MODE, int MAXU, bool TOK>
 __device__ __forceinline__ void contract_dispatch(int upw, const ContractParams& p,
                                                   unsigned char* lds, const DmaPlan& pl,
                                                   const DmaBases& bs, const ItemShape& it, int b,
@@ -807,7 +808,7 @@ __device__ __forceinline__ void contract_dispatch(int upw, const ContractParams&
                                                   const uint8_t* s_mv, const uint8_t* s_mt,
                                                   float (*s_w)[kItemRows]) {
 #define GKD_CONTRACT(U) \
-  contract_item<MODE, (U < MAXU ? U : MAXU)>(p, lds, pl, bs, it, b, wave, lane, s_rows, s_mv, \
+  contract_item<MODE, (U < MAXU ? U : MAXU), TOK>(p, lds, pl, bs, it, b, wave, lane, s_rows, s_mv, \
                                              s_mt, s_w)
   switch (upw) {
     case 1: GKD_CONTRACT(1); break;
@@ -819,6 +820,7 @@ __device__ __forceinline__ void contract_dispatch(int upw, const ContractParams&
 #undef GKD_CONTRACT
 }
 
+template <bool TOK>
 __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   extern __shared__ __align__(16) unsigned char lds[];
   __shared__ int s_rows[kItemRows];
@@ -839,7 +841,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // set-up below from being hoisted and held across the K loop
   int lane_p = lane;
   asm volatile("" : "+v"(lane_p));
-  const bool tok = p.tok_T > 0;
+  constexpr bool tok = TOK;
   ItemShape it;
   it.ng = p.ng;
   it.chunk_px = it.ng * kGroupPx;
@@ -899,7 +901,7 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
       pl.live1 |= 1u << i;
     }
   }
-  issue_features(pl, bs, lds, wave, 0, tok);
+  issue_features<TOK>(pl, bs, lds, wave, 0);
 
   if (wave == 0)
     select_rows(mv, mt, p.R, lane, rblk, kItemRows, s_rows, s_mv, s_mt, &s_nvalid, &s_nsel);
@@ -1005,22 +1007,22 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // items of the batch a larger share of the memory bandwidth, so all
   // items finish closer together.
   it.ahead = it.arows <= p.light_arows ? 1 : kStages - 1;
-  if (it.ahead > 1 && p.nsteps > 1) issue_features(pl, bs, lds + (size_t)it.fbytes, wave, 1, tok);
+  if (it.ahead > 1 && p.nsteps > 1) issue_features<TOK>(pl, bs, lds + (size_t)it.fbytes, wave, 1);
   unsigned char* const aring = lds + (size_t)kStages * it.fbytes;
   issue_rows(pl, bs, aring, 0, p.nsteps == 1);
 
   const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
   if (pre)
-    contract_dispatch<kPre, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+    contract_dispatch<kPre, kMaxMH, TOK>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                     s_w);
   else if (comb)
-    contract_dispatch<kComb, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+    contract_dispatch<kComb, kMaxMH, TOK>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                      s_w);
   else if (has_v)
-    contract_dispatch<kVis, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+    contract_dispatch<kVis, kMaxMH, TOK>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                     s_w);
   else
-    contract_dispatch<kTxt, kMaxMH>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
+    contract_dispatch<kTxt, kMaxMH, TOK>(upw, p, lds, pl, bs, it, b, wave, lane_p, s_rows, s_mv, s_mt,
                                     s_w);
 }
 
@@ -1362,8 +1364,12 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   cp.magic_w = (0x100000000ull + (uint64_t)a.W - 1) / (uint64_t)a.W;
   const long long cgrid = crops_pad * cp.items_per_crop;
   if (cgrid > INT_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(contract_kernel, dim3((unsigned)cgrid), dim3(kCThreads), sp.contract_lds,
-                     stream, cp);
+  if (a.tokens)
+    hipLaunchKernelGGL(contract_kernel<true>, dim3((unsigned)cgrid), dim3(kCThreads),
+                       sp.contract_lds, stream, cp);
+  else
+    hipLaunchKernelGGL(contract_kernel<false>, dim3((unsigned)cgrid), dim3(kCThreads),
+                       sp.contract_lds, stream, cp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || kp) return e;
 
