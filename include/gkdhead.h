@@ -47,7 +47,8 @@
  * which existing callers pass unchanged); version 3 adds the ROI stage
  * (gkd_roi_preprocess, gkd_roi_backproject); version 4 adds
  * GKD_COORDS_CORNERS; version 5 adds GKD_UPSAMPLE_CORNERS; version 6 adds
- * GKD_QUERY_TOKENS.
+ * GKD_QUERY_TOKENS; version 7 accepts it in gkd_vkp_pool for the support
+ * map.
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 6
+#define GKD_ABI_VERSION 7
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
@@ -78,7 +79,9 @@ extern "C" {
  * bits 8..15 via GKD_QUERY_SKIP. Needs bfloat16 features, C % 32 == 0 and
  * H*W % 16 == 0 (H*W <= 576 for keypoints only), else
  * GKD_ERR_UNSUPPORTED. The results equal, bit for bit, those of the same
- * call on the [B, C, H, W] layout. */
+ * call on the [B, C, H, W] layout. gkd_vkp_pool takes the same flag for its
+ * support map (any dtype and shape; it then runs the general VKP kernel,
+ * whose results agree with the fast one's within rounding). */
 #define GKD_QUERY_TOKENS 0x8u
 #define GKD_QUERY_SKIP(n) (((uint32_t)(n) & 255u) << 8)
 
@@ -128,7 +131,8 @@ GKD_API const char *gkd_last_error(void);
  * over the whole H x W grid, rounded to `dtype` (bf16: nearest, ties to
  * even). Rows with kpt_valid == 0 are not written.
  *
- *   support    [B,C,H,W] dtype   support feature map
+ *   support    [B,C,H,W] dtype   support feature map (or, with
+ *                                GKD_QUERY_TOKENS, [B, skip + H*W, C] tokens)
  *   kpts_px    [B,R,2]   float32 (x, y) in input pixels; the input spans
  *                                [0, W*stride_px) x [0, H*stride_px)
  *   kpt_valid  [B,R]     uint8   nonzero = row has a keypoint

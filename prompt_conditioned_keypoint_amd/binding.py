@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
-GKD_ABI_VERSION = 6          # include/gkdhead.h
+GKD_ABI_VERSION = 7          # include/gkdhead.h
 GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
 GKD_UPSAMPLE_CORNERS = 0x2   # gkd_kernel_heatmap flag: align_corners=True upsample
 GKD_COORDS_CORNERS = 0x4     # decode flag: corner-aligned -1..1 coordinates
@@ -105,13 +105,24 @@ def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
 
 def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
              stride: float = 16.0, sigma: float = 14.0,
-             out: torch.Tensor | None = None) -> torch.Tensor:
+             out: torch.Tensor | None = None, token_hw=None,
+             token_skip: int = 0) -> torch.Tensor:
     """support [B,C,H,W] (f32|bf16), kpts [B,R,2] f32 px, kpt_valid [B,R] u8
     -> protos [B,R,C] in the support dtype (rows with kpt_valid == 0 are
-    left as they are in `out`)."""
+    left as they are in `out`). token_hw=(H, W): the support map is the
+    ViT's token sequence [B, token_skip + H*W, C] (GKD_QUERY_TOKENS)."""
     lib = load()
-    _dev(support, "support", ndim=4)
-    B, C, H, W = support.shape
+    if token_hw is None:
+        _dev(support, "support", ndim=4)
+        B, C, H, W = support.shape
+        flags = 0
+    else:
+        _dev(support, "support", ndim=3)
+        H, W = (int(v) for v in token_hw)
+        B, T, C = support.shape
+        if not 0 <= token_skip <= 255 or T != token_skip + H * W:
+            raise ValueError("support must be [B, token_skip + H*W, C] with 0 <= token_skip <= 255")
+        flags = GKD_QUERY_TOKENS | (token_skip << 8)
     _dev(kpts, "kpts", torch.float32, 3)
     _dev(kpt_valid, "kpt_valid", torch.uint8, 2)
     R = kpt_valid.shape[1]
@@ -123,7 +134,7 @@ def vkp_pool(support: torch.Tensor, kpts: torch.Tensor, kpt_valid: torch.Tensor,
     if out.shape != (B, R, C):
         raise ValueError("out must be [B,R,C]")
     _check(lib.gkd_vkp_pool(_ptr(support), _ptr(kpts), _ptr(kpt_valid), B, C, H, W, R,
-                            float(stride), float(sigma), _dtype_code(support), 0,
+                            float(stride), float(sigma), _dtype_code(support), flags,
                             _ptr(out), _stream(support.device)))
     return out
 

@@ -63,7 +63,10 @@ const char* gkd_last_error(void) { return g_err; }
 gkd_status gkd_vkp_pool(const void* support, const float* kpts_px, const uint8_t* kpt_valid,
                         int B, int C, int H, int W, int R, float stride_px, float sigma_px,
                         gkd_dtype dtype, uint32_t flags, void* protos, hipStream_t stream) {
-  if (flags != 0) return fail(GKD_ERR_UNSUPPORTED, "gkd_vkp_pool: flags must be 0");
+  const bool tokens = (flags & GKD_QUERY_TOKENS) != 0;
+  const int skip = (int)((flags >> 8) & 255u);
+  if ((flags & ~(uint32_t)(GKD_QUERY_TOKENS | GKD_QUERY_SKIP(255))) != 0 || (!tokens && skip != 0))
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_vkp_pool: unknown flags 0x%x", (unsigned)flags);
   if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
     return fail(GKD_ERR_DTYPE, "gkd_vkp_pool: unknown dtype %d", (int)dtype);
   if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1)
@@ -72,7 +75,7 @@ gkd_status gkd_vkp_pool(const void* support, const float* kpts_px, const uint8_t
     return fail(GKD_ERR_VALUE, "gkd_vkp_pool: stride_px must be finite and > 0");
   if (!std::isfinite(sigma_px) || !(sigma_px > 0.f))
     return fail(GKD_ERR_VALUE, "gkd_vkp_pool: sigma_px must be finite and > 0");
-  if ((long long)C * H * W > kMaxElems || (long long)B * C * H * W > kMaxElems ||
+  if ((long long)C * H * W > kMaxElems || (long long)B * C * ((long long)H * W + skip) > kMaxElems ||
       (long long)B * R * C > kMaxElems || (long long)B * R * 2 > kMaxElems)
     return fail(GKD_ERR_SHAPE, "gkd_vkp_pool: an element count reaches 2^31");
   if (B == 0 || R == 0) return ok();
@@ -93,6 +96,8 @@ gkd_status gkd_vkp_pool(const void* support, const float* kpts_px, const uint8_t
   a.sigma = sigma_px;
   a.bf16 = dtype == GKD_DTYPE_BF16;
   a.protos = protos;
+  a.tokens = tokens;
+  a.tok_skip = skip;
   return hip_status(gkd::launch_vkp(a, stream), "gkd_vkp_pool");
 }
 

@@ -34,6 +34,8 @@ struct VkpArgs {
   float stride, sigma;
   bool bf16;
   void* protos;
+  int tok_skip;    // support as tokens [B, tok_skip + H*W, C] (channels last)
+  bool tokens;     //   when set; otherwise [B, C, H, W]
 };
 
 struct DecodeArgs {

@@ -43,6 +43,8 @@ struct VkParams {
   int cblocks, items_per_crop;
   int ldw;  // LDS row stride of the weight tile (elements)
   void* protos;
+  int tok_T, tok_skip;  // support as tokens [B, tok_T, C], pixel s at token tok_skip + s
+                        //   (tok_T == 0: [B, C, H, W]; FAST is then never used)
 };
 
 __device__ __forceinline__ float nearest_centre_offset(float x, float stride, int n) {
@@ -105,7 +107,11 @@ __global__ __launch_bounds__(kVThreads) void vkp_kernel(VkParams p) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const T* Fb = static_cast<const T*>(p.support) + (size_t)b * p.C * p.S;
+  const bool tok = p.tok_T > 0;
+  const T* Fb = static_cast<const T*>(p.support) +
+                (tok ? ((size_t)b * p.tok_T + p.tok_skip) * p.C : (size_t)b * p.C * p.S);
+  // element (channel c, pixel s) of the crop's map
+  auto at = [&](int c, int s) { return tok ? (size_t)s * p.C + c : (size_t)c * p.S + s; };
   constexpr bool kBf16 = sizeof(T) == 2;
 
   for (int s0 = 0; s0 < p.S; s0 += kVChunk) {
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(kVThreads) void vkp_kernel(VkParams p) {
             } else {
               uint16_t h[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) h[e] = (s + e < p.S) ? F[(size_t)c * p.S + s + e] : 0;
+              for (int e = 0; e < 8; ++e) h[e] = (s + e < p.S) ? F[at(c, s + e)] : 0;
               __builtin_memcpy(&v, h, 16);
             }
           }
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(kVThreads) void vkp_kernel(VkParams p) {
               bv[t] = *reinterpret_cast<const f32x4*>(F + (size_t)c * p.S + s);
             } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) bv[t][e] = (s + e < p.S) ? F[(size_t)c * p.S + s + e] : 0.f;
+              for (int e = 0; e < 4; ++e) bv[t][e] = (s + e < p.S) ? F[at(c, s + e)] : 0.f;
             }
           }
         }
@@ -564,7 +570,7 @@ hipError_t launch_t(const VkParams& p, size_t lds, int grid, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
-  if (a.bf16 && a.W <= kFMaxHW && a.H <= kFMaxHW && a.W % 8 == 0 && a.C % 16 == 0 &&
+  if (!a.tokens && a.bf16 && a.W <= kFMaxHW && a.H <= kFMaxHW && a.W % 8 == 0 && a.C % 16 == 0 &&
       a.R <= kFMaxR) {
     VkFastParams f;
     f.C = a.C;
@@ -615,6 +621,8 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
   p.stride = a.stride;
   p.inv2s2 = 1.f / (2.f * a.sigma * a.sigma);
   p.protos = a.protos;
+  p.tok_T = a.tokens ? a.tok_skip + p.S : 0;
+  p.tok_skip = a.tokens ? a.tok_skip : 0;
   p.cblocks = (a.C + kVCh - 1) / kVCh;
   const int rblocks = (a.R + kVRows - 1) / kVRows;
   p.items_per_crop = rblocks * p.cblocks;
@@ -631,9 +639,9 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
   const long long grid = (long long)crops_pad * p.items_per_crop;
   if (grid > INT_MAX) return hipErrorInvalidConfiguration;
   if (a.bf16)
-    return (p.S % 32 == 0) ? launch_t<uint16_t, true>(p, lds, (int)grid, stream)
-                           : launch_t<uint16_t, false>(p, lds, (int)grid, stream);
-  return (p.S % 16 == 0) ? launch_t<float, true>(p, lds, (int)grid, stream)
+    return (p.S % 32 == 0 && !a.tokens) ? launch_t<uint16_t, true>(p, lds, (int)grid, stream)
+                                        : launch_t<uint16_t, false>(p, lds, (int)grid, stream);
+  return (p.S % 16 == 0 && !a.tokens) ? launch_t<float, true>(p, lds, (int)grid, stream)
                          : launch_t<float, false>(p, lds, (int)grid, stream);
 }
 

@@ -53,7 +53,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 6
+    assert lib.gkd_abi_version() == 7
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
@@ -126,6 +126,8 @@ def test_kernel_heatmap_empty_batch_is_ok(lib, kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(flags=7), UNSUP),
+    (dict(flags=0x200), UNSUP),          # a token skip count without token layout
+    (dict(flags=0x10), UNSUP),
     (dict(dtype=5), DTYPE),
     (dict(C=0), SHAPE),
     (dict(B=-1), SHAPE),

@@ -744,3 +744,32 @@ def test_query_tokens_longtail(gkd):
     assert torch.equal(h0.view(torch.int32)[valid], h1.view(torch.int32)[valid])
     for a, b in zip(d0, d1):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 64, 5, 7, 9), (3, 128, 24, 24, 80), (2, 32, 6, 8, 20)])
+def test_support_tokens_layout(gkd, ora, dtype, shape):
+    """gkd_vkp_pool with the support map as tokens [B, 5 + H*W, C]: the
+    oracle's prototypes within the prototype tolerance, and bit for bit the
+    channel-row call where that call takes the same (general) kernel."""
+    B, C, H, W, R = shape
+    rng = np.random.default_rng(B + C + H + W + R)
+    s = rng.standard_normal((B, C, H, W)).astype(np.float32)
+    if dtype == "bf16":
+        s = gkdsynth.round_bf16_f32(s)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kp = rng.uniform(0, [W * 16, H * 16], size=(B, R, 2)).astype(np.float32)
+    mv = (rng.random((B, R)) < 0.7).astype(np.uint8)
+    tok = _tokens(s, 5, rng)
+    print(f"[tokens-vkp] {dtype} {shape}", flush=True)
+    p1 = gkd.vkp_pool(dev_tensor(tok, dt), dev_tensor(kp), dev_tensor(mv), token_hw=(H, W),
+                      token_skip=5)
+    p0 = gkd.vkp_pool(dev_tensor(s, dt), dev_tensor(kp), dev_tensor(mv))
+    torch.cuda.synchronize()
+    op = ora.vkp_pool(s, kp, mv, 16.0, 14.0, dtype=dtype)
+    check_protos(p1.float().cpu().numpy(), op, mv, dtype, np.abs(s).reshape(B, -1).max(1))
+    general = not (dtype == "bf16" and W <= 32 and H <= 32 and W % 8 == 0 and C % 16 == 0)
+    if general:
+        v = torch.from_numpy(mv > 0).cuda()
+        iv = torch.int16 if dtype == "bf16" else torch.int32
+        assert torch.equal(p0.view(iv)[v], p1.view(iv)[v])
