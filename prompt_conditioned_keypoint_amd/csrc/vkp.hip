@@ -254,7 +254,14 @@ struct VkFastParams {
   int cblocks;
   bool mask_words;  // R % 4 == 0 and the mask base 4-byte aligned
   uint16_t* protos;
+  int tok_T, tok_skip;  // TOK kernels: support as tokens [B, tok_T, C], pixel s at tok_skip + s
 };
+
+// Token layout (TOK): a wave's row load brings 8 channels of one pixel per
+// lane (lane = 2 j + half: pixel j, channels 8 half .. + 7 of the wave's 16);
+// the row goes through the wave's LDS slice (pixel rows of kFTokRow bytes)
+// and comes back through transposing reads as 8 pixels of one channel.
+constexpr int kFTokRow = 48;  // 16 channels (32 B) + one pad slot
 
 // Workgroup barrier without a memory fence: the row loads already in
 // flight keep streaming (this wave's LDS writes are completed first).
@@ -317,7 +324,10 @@ __device__ __forceinline__ int count_valid(const VkFastParams& p, int b) {
 // base; lane (n16, g4) adds a fixed byte offset for channel n16 and columns
 // 8 g4 .. 8 g4 + 7 (lanes past the row's columns re-read column 0 and
 // contribute zeros).
+template <bool TOK>
 __device__ __forceinline__ const char* item_base(const VkFastParams& p, int b, int c0) {
+  if constexpr (TOK)
+    return reinterpret_cast<const char*>(p.support + ((size_t)b * p.tok_T + p.tok_skip) * p.C + c0);
   return reinterpret_cast<const char*>(p.support + ((size_t)b * p.C + c0) * p.S);
 }
 __device__ __forceinline__ u32x4 load_row(const char* base, uint32_t loff) {
@@ -330,7 +340,7 @@ __device__ __forceinline__ u32x4 load_row(const char* base, uint32_t loff) {
 // 0 .. kFDepth-1 of the next item: the refill of slot d in the last period
 // is exactly the next item's row d. Without nsrc the tail refills re-read
 // the last row and the caller loads the next ring itself.
-template <int MT>
+template <int MT, bool TOK>
 __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int c0, int nsel,
                                               const char* src, uint32_t loff,
                                               bool col_ok, const char* nsrc,
@@ -339,7 +349,7 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
                                               const uint16_t (*s_wxh)[kFMaxHW],
                                               const uint16_t (*s_wxl)[kFMaxHW],
                                               const float (*s_wy)[kFRows], const float* s_inv,
-                                              int lane_in) {
+                                              int lane_in, unsigned char* tok_slice) {
   // the lane-derived LDS addresses are built here, per item, rather than
   // hoisted out of the item loop and held live across it
   int lane = lane_in;
@@ -363,12 +373,31 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
       if (i < p.H) {
         const u32x4 v = col_ok ? ring[d] : u32x4{0u, 0u, 0u, 0u};
         const int ni = i + kFDepth;
-        const size_t rowb = (size_t)p.W * 2;
+        const size_t rowb = TOK ? (size_t)p.W * p.C * 2 : (size_t)p.W * 2;
         const char* a = ni < p.H ? src + ni * rowb
                         : nsrc   ? nsrc + (ni - p.H) * rowb
                                  : src + (p.H - 1) * rowb;
         ring[d] = load_row(a, loff);
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, v);
+        bf16x8 bv;
+        if constexpr (TOK) {
+          // pixel j = lane / 2 of the row, channels 8 (lane % 2) .. + 7, to the
+          // slice; back as pixels 8 g4 .. 8 g4 + 7 of channel n16 (rows
+          // 8 g4 + n16 / 4 and + 4, columns 4 (n16 % 4) .. + 3)
+          *reinterpret_cast<u32x4*>(tok_slice + (lane >> 1) * kFTokRow + 16 * (lane & 1)) = v;
+          const uint32_t lo_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
+              tok_slice + (8 * g4 + (n16 >> 2)) * kFTokRow + 8 * (n16 & 3));
+          u32x2 lo, hi;
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %2\n"
+              "ds_read_b64_tr_b16 %1, %2 offset:%3\n"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(lo), "=&v"(hi)
+              : "v"(lo_addr), "i"(4 * kFTokRow)
+              : "memory");
+          bv = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        } else {
+          bv = __builtin_bit_cast(bf16x8, v);
+        }
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
           f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[h], bv, f32x4{0.f, 0.f, 0.f, 0.f},
@@ -394,7 +423,9 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
   }
 }
 
+template <bool TOK>
 __global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_kernel(VkFastParams p) {
+  __shared__ __align__(16) unsigned char s_tok[TOK ? kFWaves * 32 * kFTokRow : 16];
   __shared__ int s_list[kFList];  // crop << 2 | row block
   __shared__ int s_wsum[kFWaves];
   __shared__ int s_rows[kFRows];
@@ -449,9 +480,15 @@ __global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_k
   };
   decode(k, b, rblk, c0);
   bool on = c0 < p.C;
+  // TOK: lane 2 j + h loads pixel j's channels 8 h .. + 7 (pixels past W
+  // re-read pixel 0 and contribute zeros)
+  const bool tok_ok = (lane >> 1) < p.W;
   const uint32_t loff =
-      (uint32_t)(((lane & 15) * p.S + (col_ok ? 8 * g4 : 0)) * 2);
-  const char* src = item_base(p, b, on ? c0 : 0);
+      TOK ? (uint32_t)(((tok_ok ? (lane >> 1) : 0) * p.C + 8 * (lane & 1)) * 2)
+          : (uint32_t)(((lane & 15) * p.S + (col_ok ? 8 * g4 : 0)) * 2);
+  const bool row_ok = TOK ? tok_ok : col_ok;
+  unsigned char* const tok_slice = s_tok + (TOK ? (size_t)wave * 32 * kFTokRow : 0);
+  const char* src = item_base<TOK>(p, b, on ? c0 : 0);
 
   // masks and keypoints of the item's crop (registers until staged)
   uint8_t mv = 0;
@@ -466,7 +503,7 @@ __global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_k
 #pragma unroll
   for (int d = 0; d < kFDepth; ++d) {
     ring[d] = u32x4{0u, 0u, 0u, 0u};
-    if (on && d < p.H) ring[d] = load_row(src + (size_t)d * p.W * 2, loff);
+    if (on && d < p.H) ring[d] = load_row(src + (size_t)d * (TOK ? p.W * p.C : p.W) * 2, loff);
   }
 
   for (;;) {
@@ -526,7 +563,7 @@ __global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_k
     int bn = 0, rn = 0, cn = 0;
     if (has_next) decode(kn, bn, rn, cn);
     const bool on_n = has_next && cn < p.C;
-    const char* nsrc_all = on_n ? item_base(p, bn, cn) : nullptr;
+    const char* nsrc_all = on_n ? item_base<TOK>(p, bn, cn) : nullptr;
     const char* nsrc = p.chain ? nsrc_all : nullptr;
     if (has_next && tid < p.R) {
       const size_t o = (size_t)bn * p.R + tid;
@@ -536,17 +573,17 @@ __global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_k
     }
     if (on) {
       switch ((nsel + 15) / 16) {
-        case 1: vkp_fast_item<1>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
-        case 2: vkp_fast_item<2>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
-        case 3: vkp_fast_item<3>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
-        case 4: vkp_fast_item<4>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
-        default: vkp_fast_item<5>(p, b, c0, nsel, src, loff, col_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane); break;
+        case 1: vkp_fast_item<1, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 2: vkp_fast_item<2, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 3: vkp_fast_item<3, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 4: vkp_fast_item<4, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        default: vkp_fast_item<5, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
       }
     }
     if (on_n && !(on && p.chain)) {
 #pragma unroll
       for (int d = 0; d < kFDepth; ++d)
-        if (d < p.H) ring[d] = load_row(nsrc_all + (size_t)d * p.W * 2, loff);
+        if (d < p.H) ring[d] = load_row(nsrc_all + (size_t)d * (TOK ? p.W * p.C : p.W) * 2, loff);
     }
     if (!has_next) break;
     k = kn;
@@ -570,7 +607,7 @@ hipError_t launch_t(const VkParams& p, size_t lds, int grid, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
-  if (!a.tokens && a.bf16 && a.W <= kFMaxHW && a.H <= kFMaxHW && a.W % 8 == 0 && a.C % 16 == 0 &&
+  if (a.bf16 && a.W <= kFMaxHW && a.H <= kFMaxHW && a.W % 8 == 0 && a.C % 16 == 0 &&
       a.R <= kFMaxR) {
     VkFastParams f;
     f.C = a.C;
@@ -594,7 +631,10 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
     for (int b0 = 0; b0 < a.B; b0 += crops_per_launch) {
       const int nb = a.B - b0 < crops_per_launch ? a.B - b0 : crops_per_launch;
       const size_t rows0 = (size_t)b0 * a.R;
-      f.support = static_cast<const uint16_t*>(a.support) + (size_t)b0 * a.C * f.S;
+      f.tok_T = a.tokens ? a.tok_skip + f.S : 0;
+      f.tok_skip = a.tokens ? a.tok_skip : 0;
+      f.support = static_cast<const uint16_t*>(a.support) +
+                  (size_t)b0 * a.C * (a.tokens ? (size_t)f.tok_T : (size_t)f.S);
       f.kpts = a.kpts + 2 * rows0;
       f.valid = a.valid + rows0;
       f.protos = static_cast<uint16_t*>(a.protos) + rows0 * a.C;
@@ -602,7 +642,10 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
       const long long items = (long long)nb * rblocks * f.cblocks;
       const long long cap = (long long)kFWgPerCu * (cus > 0 ? cus : 1);
       const int grid = (int)(items < cap ? items : cap);
-      hipLaunchKernelGGL(vkp_fast_kernel, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
+      if (a.tokens)
+        hipLaunchKernelGGL(vkp_fast_kernel<true>, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
+      else
+        hipLaunchKernelGGL(vkp_fast_kernel<false>, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -747,11 +747,14 @@ def test_query_tokens_longtail(gkd):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(2, 64, 5, 7, 9), (3, 128, 24, 24, 80), (2, 32, 6, 8, 20)])
+@pytest.mark.parametrize("shape", [(2, 64, 5, 7, 9), (3, 128, 24, 24, 80), (2, 32, 6, 8, 20),
+                                   (2, 256, 32, 32, 40), (3, 64, 16, 16, 7)])
 def test_support_tokens_layout(gkd, ora, dtype, shape):
     """gkd_vkp_pool with the support map as tokens [B, 5 + H*W, C]: the
     oracle's prototypes within the prototype tolerance, and bit for bit the
-    channel-row call where that call takes the same (general) kernel."""
+    channel-row call (both layouts take the same kernel: the fast separable
+    one for bfloat16 maps up to 32x32 with W % 8 == 0, the general one
+    otherwise, and feed its MFMAs the same values in the same order)."""
     B, C, H, W, R = shape
     rng = np.random.default_rng(B + C + H + W + R)
     s = rng.standard_normal((B, C, H, W)).astype(np.float32)
@@ -763,13 +766,12 @@ def test_support_tokens_layout(gkd, ora, dtype, shape):
     tok = _tokens(s, 5, rng)
     print(f"[tokens-vkp] {dtype} {shape}", flush=True)
     p1 = gkd.vkp_pool(dev_tensor(tok, dt), dev_tensor(kp), dev_tensor(mv), token_hw=(H, W),
-                      token_skip=5)
-    p0 = gkd.vkp_pool(dev_tensor(s, dt), dev_tensor(kp), dev_tensor(mv))
+                      token_skip=5, out=torch.zeros((B, R, C), dtype=dt, device="cuda"))
+    p0 = gkd.vkp_pool(dev_tensor(s, dt), dev_tensor(kp), dev_tensor(mv),
+                      out=torch.zeros((B, R, C), dtype=dt, device="cuda"))
     torch.cuda.synchronize()
     op = ora.vkp_pool(s, kp, mv, 16.0, 14.0, dtype=dtype)
     check_protos(p1.float().cpu().numpy(), op, mv, dtype, np.abs(s).reshape(B, -1).max(1))
-    general = not (dtype == "bf16" and W <= 32 and H <= 32 and W % 8 == 0 and C % 16 == 0)
-    if general:
-        v = torch.from_numpy(mv > 0).cuda()
-        iv = torch.int16 if dtype == "bf16" else torch.int32
-        assert torch.equal(p0.view(iv)[v], p1.view(iv)[v])
+    v = torch.from_numpy(mv > 0).cuda()
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(p0.view(iv)[v], p1.view(iv)[v])
