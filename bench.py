@@ -303,11 +303,15 @@ def dense_mode(torch, gkd, n=50):
 def tokens_mode(torch, gkd, d, kv, mv, kt, mt, heat, dec, heat_bytes, rows, n=50):
     """The headline heatmap call with the query as the ViT's token sequence
     [B, 5 + H*W, C] (class + storage tokens first; GKD_QUERY_TOKENS), timed
-    with events like the headline call; the results equal the headline's."""
+    with events like the headline call (the results equal the headline's),
+    and the whole step with both feature maps as tokens (wall clock)."""
     B, C, H, W = d["B"], d["C"], d["H"], d["W"]
-    q = d["query"].reshape(B, C, H * W).transpose(0, 2, 1)
-    tok = np.concatenate([np.zeros((B, 5, C), np.float32), q], axis=1)
-    tok = torch.from_numpy(np.ascontiguousarray(tok)).to("cuda").to(torch.bfloat16)
+
+    def as_tokens(f):
+        t = np.concatenate([np.zeros((B, 5, C), np.float32),
+                            f.reshape(B, C, H * W).transpose(0, 2, 1)], axis=1)
+        return torch.from_numpy(np.ascontiguousarray(t)).to("cuda").to(torch.bfloat16)
+    tok = as_tokens(d["query"])
     call = lambda: gkd.kernel_heatmap(tok, kv, mv, kt, mt, out=heat, out_decode=dec,
                                       token_hw=(H, W), token_skip=5)
     for _ in range(5):
@@ -321,10 +325,29 @@ def tokens_mode(torch, gkd, d, kv, mv, kt, mt, heat, dec, heat_bytes, rows, n=50
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     gbs = heat_bytes / (ms * 1e-3) / 1e9
-    return {"note": "headline heatmap call with the query as [B, 5 + H*W, C] tokens "
-                    "(GKD_QUERY_TOKENS); not the headline",
-            "call_ms": round(ms, 4), "heatmaps_per_s_call": round(rows / (ms * 1e-3), 1),
-            "gbps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    res = {"note": "headline heatmap call (and step) with the feature maps as "
+                   "[B, 5 + H*W, C] tokens (GKD_QUERY_TOKENS); not the headline",
+           "call_ms": round(ms, 4), "heatmaps_per_s_call": round(rows / (ms * 1e-3), 1),
+           "gbps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if kv is not None and d["support"] is not None:
+        stok = as_tokens(d["support"])
+        kp = torch.from_numpy(np.nan_to_num(d["kpts"])).to("cuda")
+
+        def step():
+            gkd.vkp_pool(stok, kp, mv, d["stride"], d["sigma"], out=kv, token_hw=(H, W),
+                         token_skip=5)
+            call()
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / n
+        res["step_ms"] = round(ms_step, 4)
+        res["heatmaps_per_s"] = round(rows / (ms_step * 1e-3), 1)
+    return res
 
 
 def main():
