@@ -350,6 +350,50 @@ def tokens_mode(torch, gkd, d, kv, mv, kt, mt, heat, dec, heat_bytes, rows, n=50
     return res
 
 
+def latency_mode(torch, gkd, n=50):
+    """Latency of the small single-crop configs (launch-bound): one tiny
+    visual crop (C=256 float32, 5 valid rows) and one text crop (C=1024
+    float32, 20 valid rows), whole step (VKP when there is a visual prompt,
+    then the heatmap call with the fused decode), median of n event-timed
+    runs."""
+    import gkdsynth
+    out = {}
+    for name in ("tiny_visual", "text_f32"):
+        d = gkdsynth.make(name)
+        B, C, H, W, R = d["B"], d["C"], d["H"], d["W"], d["R"]
+        dev = "cuda"
+        q = torch.from_numpy(d["query"]).to(dev)
+        mv = torch.from_numpy(d["mask_vis"]).to(dev)
+        mt = torch.from_numpy(d["mask_txt"]).to(dev)
+        has_vis = d["support"] is not None and d["mask_vis"].any()
+        has_txt = bool(d["mask_txt"].any())
+        sup = torch.from_numpy(d["support"]).to(dev) if has_vis else None
+        kp = torch.from_numpy(np.nan_to_num(d["kpts"])).to(dev)
+        kt = torch.from_numpy(np.nan_to_num(d["kern_txt"])).to(dev)
+        protos = torch.zeros((B, R, C), device=dev)
+
+        def step():
+            if has_vis:
+                gkd.vkp_pool(sup, kp, mv, d["stride"], d["sigma"], out=protos)
+            gkd.kernel_heatmap(q, protos if has_vis else None, mv if has_vis else None,
+                               kt if has_txt else None, mt if has_txt else None)
+        for _ in range(5):
+            step()
+        evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for k in range(n):
+            evs[k][0].record()
+            step()
+            evs[k][1].record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+        out[name] = {"step_us_p10_p50_p90": [round(float(x), 1) for x in
+                                              np.percentile(us, [10, 50, 90])],
+                     "heatmaps": int(((d["mask_vis"] | d["mask_txt"]) > 0).sum())}
+    out["note"] = "single-crop configs, launch-latency bound; not the headline"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,11 +537,14 @@ def main():
         roi = roi_stage(torch, gkd, with_cpu=not args.no_cpu_baseline)
         log("[bench] dense long-tail batch")
         dense = dense_mode(torch, gkd)
+        log("[bench] small-config latency")
+        lat = latency_mode(torch, gkd)
         log("[bench] token-layout query")
         toks = tokens_mode(torch, gkd, d, protos if has_vis else None, mv if has_vis else None,
                            kt if has_txt else None, mt if has_txt else None, heat,
                            (idx, xy, score), heat_bytes, rows)
         modes = {
+            "latency_small": lat,
             "query_tokens": toks,
             "longtail_dense": dense,
             "roi_stage": roi,
