@@ -30,4 +30,7 @@ Recipe (every config):
 from .configs import CONFIGS, config_names, make, round_bf16_f32, bf16_bits
 from .roi import make_roi
 
-__all__ = ["CONFIGS", "config_names", "make", "make_roi", "round_bf16_f32", "bf16_bits"]
+from .kg import kg_weights  # noqa: E402
+
+__all__ = ["CONFIGS", "config_names", "make", "make_roi", "kg_weights", "round_bf16_f32",
+           "bf16_bits"]

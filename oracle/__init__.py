@@ -213,3 +213,6 @@ def roi_backproject(xy, boxes, image_hw, size=384):
                                    int(image_hw[0]), int(image_hw[1]), size, _ptr(out)),
            "roi_backproject")
     return out
+
+
+from .kg import kg_transformer  # noqa: E402  (pure NumPy, float64)
