@@ -350,6 +350,66 @@ def tokens_mode(torch, gkd, d, kv, mv, kt, mt, heat, dec, heat_bytes, rows, n=50
     return res
 
 
+def kg_flops(B, C, HW, R, F, nb):
+    """Algorithmic flops of the kernel-generation transformer: every slot of
+    the 2R per crop runs through every block (multiply-adds count 2)."""
+    T, M = 2 * R, B * 2 * R
+    blk = (2 * M * C * 3 * C + 4 * B * T * T * C + 2 * M * C * C      # SA
+           + 2 * M * C * C + 2 * B * HW * C * 2 * C + 4 * B * T * HW * C + 2 * M * C * C  # CA
+           + 4 * M * C * F)                                             # FFN
+    return nb * blk
+
+
+def kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows, n=20):
+    """The kernel-generation transformer (2 blocks, d_ff 1024, seeded
+    synthetic weights) on the long-tail batch: the call alone (events), and
+    the whole step VKP -> KG -> heatmap call with the fused decode (wall
+    clock), the head taking the KG's kernels."""
+    import gkdsynth
+    B, C, H, W, R = d["B"], d["C"], d["H"], d["W"], d["R"]
+    F, nb = 1024, 2
+    wt = torch.from_numpy(gkdsynth.kg_weights(C, F, nb, seed=5)).to("cuda").to(torch.bfloat16)
+    out = torch.empty((2, B, R, C), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gkd.kg_workspace_size(B, C, H, W, R, F), dtype=torch.uint8, device="cuda")
+    call = lambda: gkd.kg_transformer(q, wt, kern_vis=protos, mask_vis=mv, kern_txt=kt,
+                                      mask_txt=mt, n_blocks=nb, d_ff=F, out=out, workspace=ws)
+    for _ in range(3):
+        call()
+    evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        evs[k][0].record()
+        call()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    fl = kg_flops(B, C, H * W, R, F, nb)
+    res = {"note": "kernel-generation transformer with synthetic weights (perf only); "
+                   "not the headline",
+           "shape": {"B": B, "slots": 2 * R, "C": C, "HW": H * W, "d_ff": F, "blocks": nb,
+                     "heads": C // 64},
+           "call_ms": round(ms, 4), "alg_tflop": round(fl / 1e12, 4),
+           "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+    heat = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.float32, device="cuda")
+
+    def step():
+        gkd.vkp_pool(d["support_t"], kp, mv, d["stride"], d["sigma"], out=protos)
+        call()
+        gkd.kernel_heatmap(q, out[0], mv, out[1], mt, out=heat)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / n
+    res["step_ms"] = round(ms_step, 4)
+    res["heatmaps_per_s_with_kg"] = round(rows / (ms_step * 1e-3), 1)
+    return res
+
+
 def latency_mode(torch, gkd, n=50):
     """Latency of the small single-crop configs (launch-bound): one tiny
     visual crop (C=256 float32, 5 valid rows) and one text crop (C=1024
@@ -537,6 +597,11 @@ def main():
         roi = roi_stage(torch, gkd, with_cpu=not args.no_cpu_baseline)
         log("[bench] dense long-tail batch")
         dense = dense_mode(torch, gkd)
+        log("[bench] kernel-generation transformer")
+        kgr = None
+        if has_vis and has_txt and q.dtype == torch.bfloat16:
+            d["support_t"] = sup
+            kgr = kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows)
         log("[bench] small-config latency")
         lat = latency_mode(torch, gkd)
         log("[bench] token-layout query")
@@ -544,6 +609,7 @@ def main():
                            kt if has_txt else None, mt if has_txt else None, heat,
                            (idx, xy, score), heat_bytes, rows)
         modes = {
+            "kg_transformer": kgr,
             "latency_small": lat,
             "query_tokens": toks,
             "longtail_dense": dense,

@@ -48,7 +48,8 @@
  * (gkd_roi_preprocess, gkd_roi_backproject); version 4 adds
  * GKD_COORDS_CORNERS; version 5 adds GKD_UPSAMPLE_CORNERS; version 6 adds
  * GKD_QUERY_TOKENS; version 7 accepts it in gkd_vkp_pool for the support
- * map.
+ * map; version 8 adds the kernel-generation transformer
+ * (gkd_kg_workspace_size, gkd_kg_transformer).
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 7
+#define GKD_ABI_VERSION 8
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
@@ -276,6 +277,58 @@ GKD_API gkd_status gkd_roi_preprocess(const uint8_t *image, int height, int widt
 GKD_API gkd_status gkd_roi_backproject(const float *xy, const int32_t *boxes, int B,
                                int R, int height, int width, int out_size,
                                uint32_t flags, float *out_xy, hipStream_t stream);
+
+/*
+ * gkd_kg_transformer - the kernel-generation (KG) transformer that turns
+ * the visual and text keypoint prototypes into the kernels of the head
+ * (GKDT model card, "Architecture" bullet: 2 blocks of self- and
+ * cross-attention, d_ff = 1024, a mask token; paper summary, four-step
+ * pipeline). Readings: the sequence of a crop is its 2R slots [visual rows
+ * 0..R-1, text rows 0..R-1]; a slot whose row lacks that prompt holds the
+ * mask token; self-attention keys are the slots of rows with any prompt (a
+ * crop with none gets a zero attention output); cross-attention keys and
+ * values are the H*W query feature tokens; each block is post-norm,
+ * x = LN1(x + SA(x)), x = LN2(x + CA(x, F)), x = LN3(x + W2 relu(W1 x + b1)
+ * + b2), LayerNorm eps 1e-5; heads are 64 wide (C/64 heads), scores scaled
+ * by 1/8.
+ *
+ *   kern_vis, kern_txt [B,R,C] bf16  prototypes (NULL with their mask NULL)
+ *   mask_vis, mask_txt [B,R] u8      nonzero: the row has that prompt; at
+ *                                    least one mask must be given
+ *   query      [B,C,H,W] bf16        query features (or, with
+ *                                    GKD_QUERY_TOKENS, [B, skip + H*W, C])
+ *   weights    flat bf16             mask token [C]; then per block: SA
+ *                                    in_proj W [3C,C], b [3C]; SA out_proj
+ *                                    W [C,C], b [C]; LN1 w, b [C]; CA
+ *                                    in_proj W [3C,C], b [3C]; CA out_proj
+ *                                    W [C,C], b [C]; LN2 w, b; FFN W1
+ *                                    [d_ff,C], b1 [d_ff], W2 [C,d_ff], b2
+ *                                    [C]; LN3 w, b (torch Linear layout,
+ *                                    y = x W^T + b)
+ *   out        [2,B,R,C] bf16 (out)  kernels: out[0] from the visual slots,
+ *                                    out[1] from the text slots (the head's
+ *                                    kern_vis and kern_txt as they stand)
+ *   workspace  device memory of at least gkd_kg_workspace_size() bytes,
+ *              256-byte aligned, owned by the caller; its contents on entry
+ *              do not matter and are left undefined. Calls that share a
+ *              workspace must not overlap.
+ * dtype must be GKD_DTYPE_BF16 (matrix operands in bfloat16, accumulation,
+ * softmax, LayerNorm and the residual stream in float32). Limits: C % 64
+ * == 0, d_ff % 64 == 0, 1 <= n_blocks <= 64, 2R <= 576, H*W <= 576 (the
+ * attention holds all scores of a row in registers), else
+ * GKD_ERR_UNSUPPORTED. All arrays but the masks 16-byte aligned (else
+ * GKD_ERR_ALIGN); workspace_bytes too small gives GKD_ERR_VALUE. flags: 0
+ * or GKD_QUERY_TOKENS | GKD_QUERY_SKIP(n).
+ */
+GKD_API size_t gkd_kg_workspace_size(int B, int C, int H, int W, int R, int d_ff,
+                                     uint32_t flags);
+GKD_API gkd_status gkd_kg_transformer(const void *kern_vis, const uint8_t *mask_vis,
+                                      const void *kern_txt, const uint8_t *mask_txt,
+                                      const void *query, int B, int C, int H, int W, int R,
+                                      const void *weights, int n_blocks, int d_ff,
+                                      gkd_dtype dtype, uint32_t flags, void *out,
+                                      void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

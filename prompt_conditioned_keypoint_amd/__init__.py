@@ -8,9 +8,10 @@ Calls over the C ABI of libgkdhead (include/gkdhead.h):
   roi_preprocess   detector boxes of an image -> the backbone's normalised
                    square input (crop, resize, centre pad, normalise)
   roi_backproject  -1..1 keypoints -> image coordinates
+  kg_transformer   kernel-generation transformer: prototypes -> kernels
 """
-from .binding import (GkdError, LIB_PATH, kernel_heatmap, load, peak_decode,
-                      roi_backproject, roi_preprocess, vkp_pool)
+from .binding import (GkdError, LIB_PATH, kernel_heatmap, kg_transformer, kg_workspace_size,
+                      load, peak_decode, roi_backproject, roi_preprocess, vkp_pool)
 
-__all__ = ["GkdError", "LIB_PATH", "kernel_heatmap", "load", "peak_decode",
-           "roi_backproject", "roi_preprocess", "vkp_pool"]
+__all__ = ["GkdError", "LIB_PATH", "kernel_heatmap", "kg_transformer", "kg_workspace_size",
+           "load", "peak_decode", "roi_backproject", "roi_preprocess", "vkp_pool"]

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
-GKD_ABI_VERSION = 7          # include/gkdhead.h
+GKD_ABI_VERSION = 8          # include/gkdhead.h
 GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
 GKD_UPSAMPLE_CORNERS = 0x2   # gkd_kernel_heatmap flag: align_corners=True upsample
 GKD_COORDS_CORNERS = 0x4     # decode flag: corner-aligned -1..1 coordinates
@@ -64,6 +64,11 @@ def load():
     lib.gkd_roi_preprocess.argtypes = [_P, _I, _I, _P, _I, _I, _I, _U32, _P, _P]
     lib.gkd_roi_backproject.restype = _I
     lib.gkd_roi_backproject.argtypes = [_P, _P, _I, _I, _I, _I, _I, _U32, _P, _P]
+    lib.gkd_kg_workspace_size.restype = ctypes.c_size_t
+    lib.gkd_kg_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _U32]
+    lib.gkd_kg_transformer.restype = _I
+    lib.gkd_kg_transformer.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I,
+                                       _U32, _P, _P, ctypes.c_size_t, _P]
     if lib.gkd_abi_version() != GKD_ABI_VERSION:
         raise ImportError("libgkdhead ABI version mismatch")
     _lib = lib
@@ -284,4 +289,64 @@ def roi_backproject(xy: torch.Tensor, boxes: torch.Tensor, image_hw, size: int =
             raise ValueError("out must be [B,R,2]")
     _check(lib.gkd_roi_backproject(_ptr(xy), _ptr(boxes), B, R, int(image_hw[0]),
                                    int(image_hw[1]), size, 0, _ptr(out), _stream(xy.device)))
+    return out
+
+
+def kg_workspace_size(B: int, C: int, H: int, W: int, R: int, d_ff: int = 1024,
+                      tokens: bool = False) -> int:
+    """Bytes of workspace gkd_kg_transformer needs for these sizes."""
+    return int(load().gkd_kg_workspace_size(B, C, H, W, R, d_ff,
+                                            GKD_QUERY_TOKENS if tokens else 0))
+
+
+def kg_transformer(query: torch.Tensor, weights: torch.Tensor, kern_vis=None, mask_vis=None,
+                   kern_txt=None, mask_txt=None, n_blocks: int = 2, d_ff: int = 1024,
+                   token_hw=None, token_skip: int = 0, out=None,
+                   workspace=None) -> torch.Tensor:
+    """Kernel-generation transformer: prototypes [B,R,C] bf16 (with their
+    [B,R] u8 masks) -> kernels [2,B,R,C] bf16: out[0] from the visual slots,
+    out[1] from the text slots, ready as the heatmap call's kern_vis and
+    kern_txt.
+    query [B,C,H,W] bf16, or with token_hw=(H, W) the token sequence
+    [B, token_skip + H*W, C]; weights: the flat bf16 array. workspace: a
+    uint8 CUDA tensor of at least kg_workspace_size() bytes (allocated here
+    when None)."""
+    lib = load()
+    if token_hw is None:
+        _dev(query, "query", torch.bfloat16, 4)
+        B, C, H, W = query.shape
+        flags = 0
+    else:
+        _dev(query, "query", torch.bfloat16, 3)
+        H, W = (int(v) for v in token_hw)
+        B, T, C = query.shape
+        if not 0 <= token_skip <= 255 or T != token_skip + H * W:
+            raise ValueError("query must be [B, token_skip + H*W, C] with 0 <= token_skip <= 255")
+        flags = GKD_QUERY_TOKENS | (token_skip << 8)
+    _dev(weights, "weights", torch.bfloat16, 1)
+    masks = [m for m in (mask_vis, mask_txt) if m is not None]
+    if not masks:
+        raise ValueError("give mask_vis, mask_txt or both")
+    R = masks[0].shape[1]
+    for k, m, name in ((kern_vis, mask_vis, "vis"), (kern_txt, mask_txt, "txt")):
+        if m is None:
+            continue
+        _dev(m, "mask_" + name, torch.uint8, 2)
+        _dev(k, "kern_" + name, torch.bfloat16, 3)
+        if m.shape != (B, R) or k.shape != (B, R, C):
+            raise ValueError(f"kern_{name} must be [B,R,C] and mask_{name} [B,R]")
+    if out is None:
+        out = torch.empty((2, B, R, C), dtype=torch.bfloat16, device=query.device)
+    _dev(out, "out", torch.bfloat16, 4)
+    if out.shape != (2, B, R, C):
+        raise ValueError("out must be [2,B,R,C]")
+    need = int(lib.gkd_kg_workspace_size(B, C, H, W, R, d_ff, flags))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
+    _dev(workspace, "workspace", torch.uint8, 1)
+    _check(lib.gkd_kg_transformer(
+        _ptr(kern_vis) if mask_vis is not None else None, _ptr(mask_vis),
+        _ptr(kern_txt) if mask_txt is not None else None, _ptr(mask_txt), _ptr(query),
+        B, C, H, W, R, _ptr(weights), n_blocks, d_ff, 1, flags, _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream(query.device)))
     return out

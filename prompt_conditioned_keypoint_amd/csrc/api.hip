@@ -270,4 +270,69 @@ gkd_status gkd_roi_backproject(const float* xy, const int32_t* boxes, int B, int
   return hip_status(gkd::launch_backproject(a, stream), "gkd_roi_backproject");
 }
 
+size_t gkd_kg_workspace_size(int B, int C, int H, int W, int R, int d_ff, uint32_t flags) {
+  if (B < 0 || R < 0 || C < 64 || H < 1 || W < 1 || d_ff < 64) return 0;
+  return gkd::kg_workspace_bytes(B, C, H, W, R, d_ff, (flags & GKD_QUERY_TOKENS) != 0);
+}
+
+gkd_status gkd_kg_transformer(const void* kern_vis, const uint8_t* mask_vis, const void* kern_txt,
+                              const uint8_t* mask_txt, const void* query, int B, int C, int H,
+                              int W, int R, const void* weights, int n_blocks, int d_ff,
+                              gkd_dtype dtype, uint32_t flags, void* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  const bool tokens = (flags & GKD_QUERY_TOKENS) != 0;
+  const int skip = (int)((flags >> 8) & 255u);
+  if ((flags & ~(uint32_t)(GKD_QUERY_TOKENS | GKD_QUERY_SKIP(255))) != 0 || (!tokens && skip != 0))
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_kg_transformer: unknown flags 0x%x", (unsigned)flags);
+  if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
+    return fail(GKD_ERR_DTYPE, "gkd_kg_transformer: unknown dtype %d", (int)dtype);
+  if (dtype != GKD_DTYPE_BF16)
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_kg_transformer: needs bfloat16 operands");
+  if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1 || d_ff < 1 || n_blocks < 1)
+    return fail(GKD_ERR_SHAPE, "gkd_kg_transformer: bad shape B=%d C=%d H=%d W=%d R=%d d_ff=%d "
+                "n_blocks=%d", B, C, H, W, R, d_ff, n_blocks);
+  if (C % 64 != 0 || d_ff % 64 != 0 || n_blocks > 64 || 2LL * R > 576 || (long long)H * W > 576)
+    return fail(GKD_ERR_UNSUPPORTED, "gkd_kg_transformer: needs C %% 64 == 0, d_ff %% 64 == 0, "
+                "n_blocks <= 64, 2R <= 576 and H*W <= 576");
+  const long long HW = (long long)H * W, M = 2LL * B * R;
+  if (M * (C > d_ff ? C : d_ff) > kMaxElems || B * (HW + skip) * C > kMaxElems ||
+      (long long)C * C * 8 + 2LL * C * d_ff > kMaxElems / n_blocks)
+    return fail(GKD_ERR_SHAPE, "gkd_kg_transformer: an element count reaches 2^31");
+  if (B == 0 || R == 0) return ok();
+  if (!query || !weights || !out || !workspace)
+    return fail(GKD_ERR_NULL, "gkd_kg_transformer: NULL pointer argument");
+  if (!mask_vis && !mask_txt)
+    return fail(GKD_ERR_NULL, "gkd_kg_transformer: give mask_vis, mask_txt or both");
+  if ((mask_vis && !kern_vis) || (mask_txt && !kern_txt))
+    return fail(GKD_ERR_NULL, "gkd_kg_transformer: a mask without its prototypes");
+  if (!aligned16(query) || !aligned16(weights) || !aligned16(out) ||
+      (mask_vis && !aligned16(kern_vis)) || (mask_txt && !aligned16(kern_txt)) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GKD_ERR_ALIGN, "gkd_kg_transformer: arrays need 16-byte alignment, the "
+                "workspace 256-byte");
+  const size_t need = gkd::kg_workspace_bytes(B, C, H, W, R, d_ff, tokens);
+  if (workspace_bytes < need)
+    return fail(GKD_ERR_VALUE, "gkd_kg_transformer: workspace of %zu bytes, needs %zu",
+                workspace_bytes, need);
+  gkd::KgArgs a;
+  a.vis = mask_vis ? kern_vis : nullptr;
+  a.mv = mask_vis;
+  a.txt = mask_txt ? kern_txt : nullptr;
+  a.mt = mask_txt;
+  a.query = query;
+  a.B = B;
+  a.C = C;
+  a.H = H;
+  a.W = W;
+  a.R = R;
+  a.tok_skip = skip;
+  a.tokens = tokens;
+  a.weights = weights;
+  a.n_blocks = n_blocks;
+  a.d_ff = d_ff;
+  a.out = out;
+  a.ws = workspace;
+  return hip_status(gkd::launch_kg(a, stream), "gkd_kg_transformer");
+}
+
 }  // extern "C"

@@ -47,13 +47,13 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"gkd_vkp_pool", "gkd_kernel_heatmap", "gkd_peak_decode", "gkd_roi_preprocess",
-            "gkd_roi_backproject"} <= set(names)
+            "gkd_roi_backproject", "gkd_kg_workspace_size", "gkd_kg_transformer"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 7
+    assert lib.gkd_abi_version() == 8
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
@@ -243,3 +243,49 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         b.load()
+
+
+WS = 1 << 40   # a workspace size that passes the size check
+
+
+def kg(lib, vis=A, mv=A2, txt=None, mt=None, query=A3, B=2, C=128, H=24, W=24, R=80,
+       weights=A, nb=2, F=1024, dtype=1, flags=0, out=A2, ws=A3, ws_bytes=WS):
+    return lib.gkd_kg_transformer(vis, mv, txt, mt, query, B, C, H, W, R, weights, nb, F, dtype,
+                                  flags, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=1), UNSUP),
+    (dict(flags=0x200), UNSUP),                # a skip without the token layout
+    (dict(dtype=2), DTYPE),
+    (dict(dtype=0), UNSUP),                    # float32 operands
+    (dict(C=96), UNSUP),
+    (dict(F=100), UNSUP),
+    (dict(R=289), UNSUP),                      # 2R > 576
+    (dict(H=25), UNSUP),                       # H*W > 576
+    (dict(nb=0), SHAPE),
+    (dict(nb=65), UNSUP),
+    (dict(B=-1), SHAPE),
+    (dict(query=None), NULL),
+    (dict(weights=None), NULL),
+    (dict(out=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(mv=None), NULL),                     # no mask at all
+    (dict(vis=None), NULL),                    # a mask without its prototypes
+    (dict(query=A3 + 2), ALIGN),
+    (dict(out=A2 + 8), ALIGN),
+    (dict(ws=A3 + 16), ALIGN),
+    (dict(ws_bytes=1000), VALUE),
+])
+def test_kg_transformer_rejects(lib, kw, status):
+    assert kg(lib, **kw) == status
+    assert lib.gkd_last_error().decode() != ""
+
+
+def test_kg_transformer_empty_batch_is_ok_and_workspace_grows(lib):
+    assert kg(lib, B=0, query=None, out=None, ws=None) == OK
+    small = lib.gkd_kg_workspace_size(8, 1024, 24, 24, 80, 1024, 0)
+    big = lib.gkd_kg_workspace_size(256, 1024, 24, 24, 80, 1024, 0)
+    tok = lib.gkd_kg_workspace_size(256, 1024, 24, 24, 80, 1024, 0x8)
+    assert 0 < small < big and tok < big
+    assert lib.gkd_kg_workspace_size(2, 32, 24, 24, 80, 1024, 0) == 0

@@ -1,0 +1,136 @@
+"""GPU parity of the kernel-generation transformer (gkd_kg_transformer, HIP
+through the C ABI) against the float64 oracle on the same seeded inputs.
+
+Tolerance, from the arithmetic: the kernels round every matrix operand to
+bfloat16 (unit roundoff u = 2^-9), i.e. the block input, Q, K, V, the
+attention probabilities, the attention output and the FFN hidden layer,
+and the final kernels once more. Each rounding adds an independent error
+of at most u relative; about 8 of them per block reach an output, and
+LayerNorm keeps the outputs at unit scale, so over 2 blocks the RMS error
+is about u * sqrt(16 / 3) ~ 0.005. 3x that (0.015) bounds the RMS error, and
+0.1 (about 6 sigma of the same estimate at the largest output magnitudes
+of ~5) the largest one. A wrong head, mask or slot puts errors of order 1
+on whole rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gkdsynth
+from parity_util import dev_tensor
+
+pytestmark = pytest.mark.gpu
+
+TOL_RMS = 0.015
+TOL_MAX = 0.1
+
+
+@pytest.fixture(scope="module")
+def gkd():
+    import prompt_conditioned_keypoint_amd as m
+    m.load()
+    assert torch.cuda.is_available()
+    return m
+
+
+@pytest.fixture(scope="module")
+def okg():
+    from oracle import kg
+    return kg
+
+
+def case(seed, B, R, C, H, W, F, nb, p_vis=0.7, p_txt=0.6):
+    rng = np.random.default_rng(seed)
+    vis = gkdsynth.round_bf16_f32(rng.standard_normal((B, R, C)).astype(np.float32))
+    txt = gkdsynth.round_bf16_f32(rng.standard_normal((B, R, C)).astype(np.float32))
+    mv = (rng.random((B, R)) < p_vis).astype(np.uint8)
+    mt = (rng.random((B, R)) < p_txt).astype(np.uint8)
+    q = gkdsynth.round_bf16_f32(rng.standard_normal((B, C, H, W)).astype(np.float32))
+    w = gkdsynth.kg_weights(C, F, nb, seed=seed + 1)
+    return vis, mv, txt, mt, q, w
+
+
+def bf(x):
+    return dev_tensor(np.ascontiguousarray(x)).to(torch.bfloat16)
+
+
+def run(gkd, vis, mv, txt, mt, q, w, nb, F, tokens_skip=None):
+    if tokens_skip is None:
+        query, kw = bf(q), {}
+    else:
+        B, C = q.shape[:2]
+        tok = q.reshape(B, C, -1).transpose(0, 2, 1)
+        lead = np.full((B, tokens_skip, C), 7.0, np.float32)
+        query = bf(np.concatenate([lead, tok], axis=1))
+        kw = dict(token_hw=q.shape[2:], token_skip=tokens_skip)
+    out = gkd.kg_transformer(query, bf(w), kern_vis=bf(vis), mask_vis=dev_tensor(mv),
+                             kern_txt=bf(txt), mask_txt=dev_tensor(mt), n_blocks=nb, d_ff=F, **kw)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    return np.concatenate([o[0], o[1]], axis=1)   # [B, 2R, C] slot order
+
+
+def check(got, want):
+    err = np.abs(got - want)
+    rms = float(np.sqrt(np.mean(err ** 2)))
+    assert np.all(np.isfinite(got))
+    assert rms <= TOL_RMS, (rms, float(err.max()))
+    assert err.max() <= TOL_MAX, (rms, float(err.max()), np.unravel_index(err.argmax(), err.shape))
+
+
+@pytest.mark.parametrize("B,R,C,H,W,F", [(3, 7, 128, 5, 7, 192), (2, 40, 192, 9, 9, 128),
+                                         (1, 3, 64, 1, 1, 64)])
+def test_kg_matches_oracle_small(gkd, okg, B, R, C, H, W, F):
+    """Ragged slot counts (14, 80, 6 of 64-query tiles), ragged key tails
+    (35, 81, 1 keys) and tiles past M and N."""
+    vis, mv, txt, mt, q, w = case(B * 100 + R, B, R, C, H, W, F, 2)
+    mv[0, -1] = mt[0, -1] = 0   # a padding row
+    print(f"[kg] small B={B} R={R} C={C} HW={H * W} F={F}", flush=True)
+    got = run(gkd, vis, mv, txt, mt, q, w, 2, F)
+    want = okg.kg_transformer(vis, mv, txt, mt, q, w, 2, F)
+    check(got, want)
+
+
+def test_kg_unprompted_crop_one_block_and_text_only(gkd, okg):
+    """A crop with no prompted row (zero self-attention), one block, and a
+    call with only the text modality."""
+    vis, mv, txt, mt, q, w = case(5, 3, 9, 128, 4, 6, 128, 1)
+    mv[1] = mt[1] = 0
+    print("[kg] unprompted crop", flush=True)
+    got = run(gkd, vis, mv, txt, mt, q, w, 1, 128)
+    want = okg.kg_transformer(vis, mv, txt, mt, q, w, 1, 128)
+    check(got, want)
+    out = gkd.kg_transformer(bf(q), bf(w), kern_txt=bf(txt), mask_txt=dev_tensor(mt),
+                             n_blocks=1, d_ff=128)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    check(np.concatenate([o[0], o[1]], axis=1),
+          okg.kg_transformer(None, None, txt, mt, q, w, 1, 128))
+
+
+def test_kg_tokens_layout_is_bit_identical(gkd):
+    vis, mv, txt, mt, q, w = case(9, 2, 11, 128, 6, 5, 128, 2)
+    print("[kg] token layout", flush=True)
+    a = run(gkd, vis, mv, txt, mt, q, w, 2, 128)
+    b = run(gkd, vis, mv, txt, mt, q, w, 2, 128, tokens_skip=5)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_kg_full_size_sampled(gkd, okg):
+    """B=256 crops, C=1024, R=80 (160 slots), 24x24 query, d_ff=1024, 2
+    blocks, launched as the benchmark launches it; the oracle recomputes 3
+    sampled crops. Two runs are bit-identical."""
+    B, R, C, H, W, F = 256, 80, 1024, 24, 24, 1024
+    vis, mv, txt, mt, q, w = case(2026, B, R, C, H, W, F, 2)
+    n = np.random.default_rng(1).integers(1, R + 1, B)
+    pad = np.arange(R)[None, :] >= n[:, None]
+    mv[pad] = 0
+    mt[pad] = 0
+    print("[kg] full size", flush=True)
+    a = run(gkd, vis, mv, txt, mt, q, w, 2, F)
+    b = run(gkd, vis, mv, txt, mt, q, w, 2, F)
+    np.testing.assert_array_equal(a, b)
+    for i in (0, 101, 255):
+        want = okg.kg_transformer(vis[i:i + 1], mv[i:i + 1], txt[i:i + 1], mt[i:i + 1],
+                                  q[i:i + 1], w, 2, F)
+        check(a[i:i + 1], want)
