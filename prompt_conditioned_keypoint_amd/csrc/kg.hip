@@ -29,7 +29,6 @@ namespace {
 constexpr int kHd = 64;          // head width
 constexpr int kMaxKeys = 576;    // attention keys held in registers (36 tiles of 16)
 constexpr int kKeyTiles = kMaxKeys / 16;
-constexpr int kPPitch = kMaxKeys + 8;  // bf16 per LDS row of probabilities (16-B rows)
 constexpr int kGT = 128;         // GEMM tile (M and N)
 constexpr int kGK = 64;          // GEMM K step
 constexpr int kGPitch = kGK + 8; // bf16 per LDS tile row (16-B aligned, skewed banks)
@@ -174,12 +173,18 @@ __global__ __launch_bounds__(256) void kg_gemm_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Attention of Tq queries over Tk <= 576 keys for one (crop, head): each
-// wave takes 16 queries, holds their 16 x Tk scores in registers (36 MFMA
-// tiles), takes the softmax with the 1/sqrt(64) scale, writes the
-// unnormalised probabilities to LDS in bfloat16, multiplies them by V^T and
-// divides by the row sums. Keys with key_ok == 0 get probability 0; a row
-// without an allowed key gives 0.
+// Attention of Tq queries over Tk <= 576 keys for one (crop, head), one
+// workgroup of 4 waves per (crop, head): K [Tk, 64] and V^T [64, Tk] of the
+// head are staged in LDS once (keys past Tk read as 0) and every wave reads
+// them there. A wave takes 16 queries at a time and computes the transposed scores S^T = K Q^T, so
+// lane (query n = lane & 15, group g = lane >> 4) holds keys 16 t + 4 g + e
+// (e = 0..3) of its query in tile t: 36 tiles cover 576 keys in registers.
+// Softmax (scale 1/sqrt(64)) reduces over e, t and the 4 lane groups. The
+// product O^T = V^T P^T then takes its P^T operand straight from those
+// registers: an MFMA sums over its 32 k-slots in any order as long as both
+// operands agree, so k-slots 8 g .. 8 g + 7 of a 32-key chunk c carry keys
+// 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3) on both sides. Keys with
+// key_ok == 0 get probability 0; a query without an allowed key gives 0.
 // ---------------------------------------------------------------------------
 struct AttnParams {
   const uint16_t* q;
@@ -191,108 +196,146 @@ struct AttnParams {
   const uint8_t* key_ok;  // [B, Tk], or null: every key
   uint16_t* out;
   int ldo;
-  int nh, Tq, Tk, qtiles;
+  int nh, Tq, Tk;
 };
 
-__global__ __launch_bounds__(256) void kg_attn_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sP[4][16 * kPPitch];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int qt = blockIdx.x % p.qtiles, bh = blockIdx.x / p.qtiles;
-  const int h = bh % p.nh, b = bh / p.nh;
-  const int q0 = qt * 64 + wave * 16;
+constexpr int kAttnWaves = 4;
+constexpr int kKPitch = kHd + 8;  // bf16 per LDS row of K (16-B rows, skewed banks)
+
+__host__ __device__ inline int attn_vpitch(int Tk) { return rup32(Tk) + 8; }
+__host__ __device__ inline size_t attn_lds_bytes(int Tk) {
+  return (size_t)((Tk + 15) & ~15) * kKPitch * 2 + (size_t)kHd * attn_vpitch(Tk) * 2;
+}
+
+// bfloat16 bits of a float, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// NT: key tiles held in registers (10 covers 160 keys, 36 covers 576).
+template <int NT>
+__global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds_kv[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x % p.nh, b = blockIdx.x / p.nh;
   const int fr = lane & 15, g = lane >> 4, fk = g * 8;
-  const int nt = (p.Tk + 15) >> 4, kpad = rup32(p.Tk);
+  const int nt = (p.Tk + 15) >> 4, kpad = rup32(p.Tk), vp = attn_vpitch(p.Tk);
+  uint16_t* sK = lds_kv;
+  uint16_t* sV = lds_kv + (size_t)nt * 16 * kKPitch;
+
+  // Stage K (rows of 8 16-byte pieces) and V^T (64 rows of kpad keys).
+  for (int c = tid; c < p.Tk * 8; c += 64 * kAttnWaves) {
+    const int key = c >> 3, piece = (c & 7) * 8;
+    *reinterpret_cast<u32x4*>(&sK[key * kKPitch + piece]) = *reinterpret_cast<const u32x4*>(
+        p.k + (long long)(b * p.Tk + key) * p.ldk + h * kHd + piece);
+  }
+  const uint16_t* vsrc = p.vt + (long long)(b * p.nh + h) * kHd * p.vt_ld;
+  for (int c = tid; c < kHd * (kpad / 8); c += 64 * kAttnWaves) {
+    const int d = c / (kpad / 8), k8 = (c % (kpad / 8)) * 8;
+    const uint16_t* src = vsrc + (long long)d * p.vt_ld + k8;
+    u32x4 v;
+    if (k8 + 8 <= p.Tk) {
+      v = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (k8 + 2 * e < p.Tk ? (uint32_t)src[2 * e] : 0u) |
+               ((k8 + 2 * e + 1 < p.Tk ? (uint32_t)src[2 * e + 1] : 0u) << 16);
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    *reinterpret_cast<u32x4*>(&sV[d * vp + k8]) = v;
+  }
+  __syncthreads();
+
+  for (int q0 = wave * 16; q0 < p.Tq; q0 += 16 * kAttnWaves) {
 
   const uint16_t* qrow = p.q + (long long)(b * p.Tq + min(q0 + fr, p.Tq - 1)) * p.ldq + h * kHd + fk;
-  const bf16x8 qa0 = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow));
-  const bf16x8 qa1 = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32));
+  const bf16x8 qb0 = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow));
+  const bf16x8 qb1 = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32));
+  const uint8_t* okrow = p.key_ok ? p.key_ok + (long long)b * p.Tk : nullptr;
 
-  f32x4 s[kKeyTiles];
-  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  uint32_t okbits[2] = {0u, 0u};  // bit t: this lane's key of tile t is allowed
+  f32x4 s[NT];
+  float mx = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < kKeyTiles; ++t) {
+  for (int t = 0; t < NT; ++t) {
     if (t < nt) {
-      const int key = t * 16 + fr;
-      const uint16_t* krow = p.k + (long long)(b * p.Tk + min(key, p.Tk - 1)) * p.ldk + h * kHd + fk;
+      const uint16_t* krow = sK + (t * 16 + fr) * kKPitch + fk;  // rows past Tk: masked below
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, as_bf16x8(*reinterpret_cast<const u32x4*>(krow)), z, 0, 0, 0);
-      s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32)), z, 0, 0, 0);
-      const bool ok = key < p.Tk && (!p.key_ok || p.key_ok[(long long)b * p.Tk + key]);
-      if (ok) {
-        okbits[t >> 5] |= 1u << (t & 31);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx[e] = fmaxf(mx[e], s[t][e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], d));
-
-  // p = exp((s - max) / 8) = exp2((s - max) * log2(e) / 8)
-  constexpr float kScale = 0.125f * 1.4426950408889634f;
-  float sum[4] = {0.f, 0.f, 0.f, 0.f};
-  uint16_t* myP = sP[wave];
-#pragma unroll
-  for (int t = 0; t < kKeyTiles; ++t) {
-    if (t < nt) {
-      const bool ok = (okbits[t >> 5] >> (t & 31)) & 1u;
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(krow)), qb0, z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32)), qb1, z, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v = ok ? exp2f((s[t][e] - mx[e]) * kScale) : 0.f;
-        const uint16_t hb = f32_to_bf16_bits(v);
-        sum[e] += bf16_bits_to_f32(hb);  // the sum of what the product uses
-        myP[(4 * g + e) * kPPitch + t * 16 + fr] = hb;
+        const int key = t * 16 + 4 * g + e;
+        const bool ok = key < p.Tk && (!okrow || okrow[key]);
+        z[e] = ok ? z[e] : -INFINITY;
+        mx = fmaxf(mx, z[e]);
       }
-    } else if (t * 16 < kpad) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) myP[(4 * g + e) * kPPitch + t * 16 + fr] = 0;
+      s[t] = z;
     }
   }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+  // p = exp((s - max) / 8) = exp2((s - max) * log2(e) / 8); masked keys hold
+  // -inf and give 0, and so does every key of a query with no allowed key.
+  constexpr float kScale = 0.125f * 1.4426950408889634f;
+  const float base = mx == -INFINITY ? 0.f : mx;
+  float sum = 0.f;
+  uint32_t pk[NT + 1][2];  // bfloat16 pairs: keys (4g, 4g+1), (4g+2, 4g+3) of tile t
+  pk[NT][0] = pk[NT][1] = 0u;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int t = 0; t < NT; ++t) {
+    if (t < nt) {
+      uint32_t hb[4];
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) sum[e] += __shfl_xor(sum[e], d);
-  __syncthreads();
+      for (int e = 0; e < 4; ++e) {
+        // v_exp_f32 directly: arguments are <= 0 and results below 2^-126
+        // are far under the bfloat16 rounding of the largest term.
+        hb[e] = bf16_rne(__builtin_amdgcn_exp2f((s[t][e] - base) * kScale));
+        sum += bf16_bits_to_f32(hb[e]);  // the sum of what the product uses
+      }
+      pk[t][0] = hb[0] | (hb[1] << 16);
+      pk[t][1] = hb[2] | (hb[3] << 16);
+    } else {
+      pk[t][0] = pk[t][1] = 0u;
+    }
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
 
   f32x4 o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* vbase = p.vt + (long long)(b * p.nh + h) * kHd * p.vt_ld;
-  for (int k0 = 0; k0 < kpad; k0 += 32) {
-    const bf16x8 pa = as_bf16x8(*reinterpret_cast<const u32x4*>(&myP[fr * kPPitch + k0 + fk]));
-    const int kb = k0 + fk;
+  const uint16_t* vbase = sV + 4 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint16_t* vrow = vbase + (long long)(16 * j + fr) * p.vt_ld;
-      u32x4 v;
-      if (kb + 8 <= p.Tk) {
-        v = *reinterpret_cast<const u32x4*>(vrow + kb);
-      } else {  // ragged key tail: keys past Tk contribute 0 (their p is 0 too)
-        uint32_t w[4];
+  for (int c = 0; c < (NT + 1) / 2; ++c) {
+    if (2 * c < nt) {
+      const bf16x8 pb = as_bf16x8(u32x4{pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]});
+      const int k0 = 32 * c;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = kb + 2 * e < p.Tk ? vrow[kb + 2 * e] : 0u;
-          const uint32_t hi = kb + 2 * e + 1 < p.Tk ? vrow[kb + 2 * e + 1] : 0u;
-          w[e] = lo | (hi << 16);
-        }
-        v = u32x4{w[0], w[1], w[2], w[3]};
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t* vrow = vbase + (16 * j + fr) * vp + k0;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[j], 0, 0, 0);
       }
-      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(v), o[j], 0, 0, 0);
     }
   }
-  // o[j][e] = O[query q0 + 4 g + e][dim 16 j + fr]
+  // o[j][e] = O^T[dim 16 j + 4 g + e][query q0 + fr]
+  const int qi = q0 + fr;
+  if (qi < p.Tq) {
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    uint16_t* orow = p.out + (long long)(b * p.Tq + qi) * p.ldo + h * kHd + 4 * g;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int qi = q0 + 4 * g + e;
-    if (qi >= p.Tq) continue;
-    const float inv = sum[e] > 0.f ? 1.f / sum[e] : 0.f;
-    uint16_t* orow = p.out + (long long)(b * p.Tq + qi) * p.ldo + h * kHd;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) orow[16 * j + fr] = f32_to_bf16_bits(o[j][e] * inv);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w0 = f32_to_bf16_bits(o[j][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[j][1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(o[j][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[j][3] * inv) << 16);
+      *reinterpret_cast<u32x2*>(orow + 16 * j) = u32x2{w0, w1};
+    }
   }
+  }  // query groups
 }
 
 // ---------------------------------------------------------------------------
@@ -420,9 +463,11 @@ hipError_t gemm(const uint16_t* A, long long a_bstride, int a_rows, int lda, con
 hipError_t attn(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* vt,
                 int vt_ld, const uint8_t* key_ok, uint16_t* out, int ldo, int B, int nh, int Tq,
                 int Tk, hipStream_t st) {
-  const int qtiles = (Tq + 63) / 64;
-  AttnParams p{q, ldq, k, ldk, vt, vt_ld, key_ok, out, ldo, nh, Tq, Tk, qtiles};
-  hipLaunchKernelGGL(kg_attn_kernel, dim3(B * nh * qtiles), dim3(256), 0, st, p);
+  AttnParams p{q, ldq, k, ldk, vt, vt_ld, key_ok, out, ldo, nh, Tq, Tk};
+  if (Tk <= 160)
+    hipLaunchKernelGGL(kg_attn_kernel<10>, dim3(B * nh), dim3(64 * kAttnWaves), attn_lds_bytes(Tk), st, p);
+  else
+    hipLaunchKernelGGL(kg_attn_kernel<kKeyTiles>, dim3(B * nh), dim3(64 * kAttnWaves), attn_lds_bytes(Tk), st, p);
   return hipGetLastError();
 }
 
