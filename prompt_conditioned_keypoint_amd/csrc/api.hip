@@ -5,6 +5,7 @@
 // nothing, writes nothing and does not even touch the HIP runtime.
 #include "gkdhead.h"
 #include "launch.hpp"
+#include "kg_launch.hpp"
 
 #include <cmath>
 #include <cstdarg>

@@ -21,7 +21,7 @@
 //   gemm   W1 + bias, ReLU -> gemm W2 + bias + residual -> LayerNorm
 // The products run on v_mfma_f32_16x16x32_bf16.
 #include "gkd_device.hpp"
-#include "launch.hpp"
+#include "kg_launch.hpp"
 
 namespace gkd {
 namespace {

@@ -95,22 +95,4 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_roi(const RoiArgs& a, hipStream_t stream);
 hipError_t launch_backproject(const BackprojectArgs& a, hipStream_t stream);
 
-struct KgArgs {
-  const void* vis;        // [B,R,C] bf16 or null
-  const uint8_t* mv;      // [B,R] or null
-  const void* txt;        // [B,R,C] bf16 or null
-  const uint8_t* mt;      // [B,R] or null
-  const void* query;      // [B,C,H,W] bf16, or tokens [B, tok_skip + H*W, C]
-  int B, C, H, W, R;
-  int tok_skip;
-  bool tokens;
-  const void* weights;    // flat bf16 array (mask token, then per block)
-  int n_blocks, d_ff;
-  void* out;              // [2,B,R,C] bf16: visual kernels, then text kernels
-  void* ws;               // workspace of kg_workspace_bytes() bytes, 256-B aligned
-};
-
-size_t kg_workspace_bytes(int B, int C, int H, int W, int R, int d_ff, bool tokens);
-hipError_t launch_kg(const KgArgs& a, hipStream_t stream);
-
 }  // namespace gkd
