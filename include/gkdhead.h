@@ -16,7 +16,10 @@
  * and the ROI stage either side of the head in top-down use:
  *   4. gkd_roi_preprocess   crop, resize, centre-pad and normalise detector
  *                           boxes of an image into the backbone's input;
- *   5. gkd_roi_backproject  -1..1 keypoints back to image coordinates.
+ *   5. gkd_roi_backproject  -1..1 keypoints back to image coordinates;
+ * and the step that makes the kernels from the prototypes:
+ *   6. gkd_kg_transformer   the kernel-generation transformer (with
+ *                           gkd_kg_workspace_size for its workspace).
  *
  * Conventions shared by every call:
  *   - Every array argument is a DEVICE pointer owned by the caller, dense
@@ -39,8 +42,9 @@
  *   - `flags` must be 0 (else GKD_ERR_UNSUPPORTED), except for the
  *     heatmap output format, upsample grid and query layout flags of
  *     gkd_kernel_heatmap (GKD_HEATMAP_BF16, GKD_UPSAMPLE_CORNERS,
- *     GKD_QUERY_TOKENS with GKD_QUERY_SKIP) and the keypoint coordinate
- *     flag of gkd_kernel_heatmap and gkd_peak_decode (GKD_COORDS_CORNERS).
+ *     GKD_QUERY_TOKENS with GKD_QUERY_SKIP, which gkd_vkp_pool and
+ *     gkd_kg_transformer accept too) and the keypoint coordinate flag of
+ *     gkd_kernel_heatmap and gkd_peak_decode (GKD_COORDS_CORNERS).
  *
  * ABI history: version 1 had float32 heatmaps only; version 2 adds
  * GKD_HEATMAP_BF16 (gkd_kernel_heatmap's heatmaps argument became void *,
