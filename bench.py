@@ -15,11 +15,18 @@ average duration, timed with events on the stream it runs on.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload on this host.
 
+The headline steps run back to back (steady state: each step's VKP starts
+behind the previous call's heatmap write stream). The heatmap call is also
+timed alone with a 1 GiB buffer write between calls (`cold`: nothing of
+the inputs is left in L2 or the memory-side cache), median/p10/p90 of 50.
+
   python bench.py [--steps K] [--warmup W] [--gpus 1]
   python bench.py --copy-only      # plain copy kernel of known size, for
                                    # scaling rocprofv3 byte counters
   python bench.py --no-modes       # headline only (profiling runs)
   python bench.py --roi-only       # the ROI stage only (profiling runs)
+  python bench.py --kg-only        # the KG transformer only (profiling runs)
+  python bench.py --workload dual_bf16 --no-modes   # one config's call
 """
 from __future__ import annotations
 
@@ -142,30 +149,48 @@ def copy_bandwidth(torch, nbytes=1 << 30, iters=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(d, target_s=20.0, max_crops=None):
-    """Time the oracle chain (VKP -> heatmap) on the first crops of the
-    workload until ~target_s of CPU work; return rows/s and the sample."""
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(d, gpu_protos, target_s=20.0, max_crops=None):
+    """Time the oracle on the first crops of the workload until ~target_s of
+    CPU work: VKP (the oracle's own prototypes, compared with the GPU's),
+    then the heatmaps from the GPU's prototypes (the kernels the timed GPU
+    call used, so the heatmap stage compares like with like; its cost does
+    not depend on the kernel values). Returns rows/s of the two stages
+    together, the sample, and the oracle's prototypes and heatmaps."""
     import oracle
-    t0 = time.perf_counter()
     rows = crops = 0
-    res = {}
+    t_vkp = t_heat = 0.0
+    heat, protos = {}, {}
     max_crops = d["B"] if max_crops is None else max_crops
-    while crops < min(max_crops, d["B"]) and time.perf_counter() - t0 < target_s:
+    while crops < min(max_crops, d["B"]) and t_vkp + t_heat < target_s:
         b = crops
         sl = slice(b, b + 1)
         mv, mt = d["mask_vis"][sl], d["mask_txt"][sl]
-        kv = None
+        t0 = time.perf_counter()
         if mv.any():
-            kv = oracle.vkp_pool(d["support"][sl], d["kpts"][sl], mv, d["stride"],
-                                 d["sigma"], dtype=d["dtype"])
-        heat = oracle.kernel_heatmap(d["query"][sl], kv if mv.any() else None,
-                                     mv if mv.any() else None,
-                                     d["kern_txt"][sl] if mt.any() else None,
-                                     mt if mt.any() else None)
-        res[b] = heat
+            protos[b] = oracle.vkp_pool(d["support"][sl], d["kpts"][sl], mv, d["stride"],
+                                        d["sigma"], dtype=d["dtype"])
+        t1 = time.perf_counter()
+        kv = np.nan_to_num(gpu_protos[sl]) if mv.any() else None
+        heat[b] = oracle.kernel_heatmap(d["query"][sl], kv, mv if mv.any() else None,
+                                        d["kern_txt"][sl] if mt.any() else None,
+                                        mt if mt.any() else None)
+        t2 = time.perf_counter()
+        t_vkp += t1 - t0
+        t_heat += t2 - t1
         rows += int(((mv | mt) > 0).sum())
         crops += 1
-    dt = time.perf_counter() - t0
+    dt = t_vkp + t_heat
     # and one crop on one host thread
     nthreads = oracle.max_threads()
     oracle.set_threads(1)
@@ -177,35 +202,95 @@ def cpu_baseline(d, target_s=20.0, max_crops=None):
                           d["kern_txt"][:1] if mt.any() else None, mt if mt.any() else None)
     one = time.perf_counter() - t1
     oracle.set_threads(nthreads)
-    return rows / dt, dict(crops=crops, rows=rows, seconds=dt, one_crop_1thread_s=one,
-                           one_crop_rows=int(((mv | mt) > 0).sum())), res
+    return rows / dt, dict(crops=crops, rows=rows, seconds=dt, vkp_s=t_vkp, heat_s=t_heat,
+                           one_crop_1thread_s=one,
+                           one_crop_rows=int(((mv | mt) > 0).sum())), heat, protos
 
 
-def check_parity(d, heat_gpu, dec_gpu, ora_heat):
-    """Compare the timed GPU outputs with the oracle on the sampled crops."""
+GAP_TOL = 1e-3  # the argmax contract: bit-exact where the oracle's top-2 gap exceeds it
+
+
+def check_parity(d, heat_gpu, idx_gpu, ora_heat, protos_gpu=None, ora_protos=None):
+    """Compare the timed GPU outputs with the oracle on the sampled crops.
+    The oracle's heatmaps were computed from the same kernels as the GPU's
+    (its prototypes included), so the contract applies as it stands:
+    heatmaps within 2e-2 of the row maximum (bf16 features; 1e-4 absolute
+    for float32), and the index bit-exact wherever the oracle's top-2 gap
+    exceeds 1e-3, else on a cell within 1e-3 of the maximum; a row that
+    meets neither counts as a mismatch. The prototypes are compared with
+    the oracle's own within one bf16 ulp (plus 1e-5 max |support|)."""
     import oracle
-    worst = 0.0
+    worst = worst_abs_scaled = 0.0
     exact = near = bad = 0
+    scale = np.sqrt(d["C"])
     for b, oh in ora_heat.items():
         valid = ((d["mask_vis"][b] | d["mask_txt"][b]) > 0)
         g = heat_gpu[b]
+        fmax = np.abs(d["query"][b]).max()
         _, _, _, gap = oracle.peak_decode(np.nan_to_num(oh), valid[None].astype(np.uint8))
         o_idx, _, _, _ = oracle.peak_decode(oh.astype(np.float32).astype(np.float64),
                                             valid[None].astype(np.uint8))
         for r in np.nonzero(valid)[0]:
             o = oh[0, r]
-            err = np.abs(g[r].astype(np.float64) - o).max() / max(np.abs(o).max(), 1e-30)
-            worst = max(worst, err)
-            gi = int(dec_gpu[0][b, r])
-            if gap[0, r] > 4e-3:
+            dif = np.abs(g[r].astype(np.float64) - o).max()
+            worst = max(worst, dif / max(np.abs(o).max(), 1e-30))
+            worst_abs_scaled = max(worst_abs_scaled, dif / (scale * fmax))
+            gi = int(idx_gpu[b, r])
+            if gap[0, r] > GAP_TOL:
                 if gi == o_idx[0, r]:
                     exact += 1
                 else:
                     bad += 1
+            elif 0 <= gi < o.size and o.reshape(-1)[gi] >= o.max() - GAP_TOL:
+                near += 1
             else:
-                near += 1 if o.reshape(-1)[gi] >= o.max() - 4e-3 else 0
-    return dict(max_rel_err=float(worst), argmax_exact=exact, argmax_near_tie=near,
-                argmax_mismatch=bad, ok=bool(worst <= 2e-2 and bad == 0))
+                bad += 1
+    rel_bar = 2e-2 if d["dtype"] == "bf16" else None
+    ok = bad == 0 and (worst <= rel_bar if rel_bar else True)
+    res = dict(crops=len(ora_heat), max_rel_err=float(worst),
+               max_err_over_sqrtC_maxF=float(worst_abs_scaled),
+               argmax_exact=exact, argmax_near_tie=near, argmax_mismatch=bad,
+               gap_tol=GAP_TOL)
+    if ora_protos:
+        pw = 0.0
+        for b, op in ora_protos.items():
+            m = d["mask_vis"][b] > 0
+            gp = protos_gpu[b][m].astype(np.float64)
+            o = op[0][m]
+            ulp = np.abs(o) * 2.0 ** -7 + 1e-5 * np.abs(d["support"][b]).max()
+            pw = max(pw, float((np.abs(gp - o) / ulp).max()))
+        res["protos_err_in_ulps_max"] = round(pw, 4)
+        ok = ok and pw <= 1.0
+    res["ok"] = bool(ok)
+    return res
+
+
+def timed_calls(torch, fn, n, flush=None):
+    """Durations (ms) of n calls of fn, each bracketed by fence-free events on
+    the current stream; with flush, flush() runs between calls, outside the
+    events."""
+    evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        if flush is not None:
+            flush()
+        evs[k][0].record()
+        fn()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def make_flush(torch, nbytes=1 << 30):
+    """A 1 GiB buffer whose fill between timed calls evicts the L2s and the
+    memory-side cache (256 MB on MI355X)."""
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    return lambda: buf.fill_(1.0)
+
+
+def stats(ms):
+    return {"mean": round(float(ms.mean()), 4), "p10_p50_p90":
+            [round(float(x), 4) for x in np.percentile(ms, [10, 50, 90])]}
 
 
 def roi_stage(torch, gkd, n=50, with_cpu=True):
@@ -351,12 +436,27 @@ def tokens_mode(torch, gkd, d, kv, mv, kt, mt, heat, dec, heat_bytes, rows, n=50
 
 
 def kg_flops(B, C, HW, R, F, nb):
-    """Algorithmic flops of the kernel-generation transformer: every slot of
-    the 2R per crop runs through every block (multiply-adds count 2)."""
+    """Flops of the kernel-generation transformer if every slot of the 2R per
+    crop ran through every block (multiply-adds count 2): the padded count."""
     T, M = 2 * R, B * 2 * R
     blk = (2 * M * C * 3 * C + 4 * B * T * T * C + 2 * M * C * C      # SA
            + 2 * M * C * C + 2 * B * HW * C * 2 * C + 4 * B * T * HW * C + 2 * M * C * C  # CA
            + 4 * M * C * F)                                             # FFN
+    return nb * blk
+
+
+def kg_flops_prompted(mask_vis, mask_txt, C, HW, F, nb):
+    """Flops of the method's own work: only the 2 n_b slots of the n_b rows
+    with a prompt in crop b enter the attention and the dense layers, and
+    the query's keys and values are projected for crops with such rows."""
+    n = ((mask_vis > 0) | (mask_txt > 0)).sum(1).astype(np.int64)
+    T = 2 * n
+    M = int(T.sum())
+    crops = int((n > 0).sum())
+    blk = (2 * M * C * 3 * C + 4 * int((T * T).sum()) * C + 2 * M * C * C      # SA
+           + 2 * M * C * C + 2 * crops * HW * C * 2 * C + 4 * M * HW * C
+           + 2 * M * C * C                                                     # CA
+           + 4 * M * C * F)                                                    # FFN
     return nb * blk
 
 
@@ -384,13 +484,18 @@ def kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows, n=20):
     torch.cuda.synchronize()
     ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     fl = kg_flops(B, C, H * W, R, F, nb)
+    flp = kg_flops_prompted(d["mask_vis"], d["mask_txt"], C, H * W, F, nb)
     res = {"note": "kernel-generation transformer with synthetic weights (perf only); "
                    "not the headline",
            "shape": {"B": B, "slots": 2 * R, "C": C, "HW": H * W, "d_ff": F, "blocks": nb,
-                     "heads": C // 64},
-           "call_ms": round(ms, 4), "alg_tflop": round(fl / 1e12, 4),
-           "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-           "mfma_frac": round(fl / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+                     "heads": C // 64,
+                     "prompted_slots": int(2 * ((d["mask_vis"] | d["mask_txt"]) > 0).sum())},
+           "call_ms": round(ms, 4),
+           "alg_tflop": round(flp / 1e12, 4),
+           "tflops": round(flp / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round(flp / (ms * 1e-3) / 1e12 / 2500.0, 4),
+           "padded_tflop": round(fl / 1e12, 4),
+           "padded_tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
     heat = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.float32, device="cuda")
 
     def step():
@@ -408,6 +513,104 @@ def kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows, n=20):
     res["step_ms"] = round(ms_step, 4)
     res["heatmaps_per_s_with_kg"] = round(rows / (ms_step * 1e-3), 1)
     return res
+
+
+def config_mode(torch, gkd, name, n=50, flush=None):
+    """One workload's heatmap call at its own shape, alone: warm (calls back
+    to back) and cold (a 1 GiB write between calls, so no input byte is
+    left in L2 or the memory-side cache), median/p10/p90 of n event-timed
+    calls, rated by its algorithmic bytes; the VKP call likewise; and the
+    whole step (VKP, then the call with the fused decode), wall clock."""
+    import gkdsynth
+    d = gkdsynth.make(name)
+    heat_bytes, vkp_bytes, rows = algorithmic_bytes(d)
+    B, C, H, W, R = d["B"], d["C"], d["H"], d["W"], d["R"]
+    dev = "cuda"
+    dt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
+    q = torch.from_numpy(d["query"]).to(dev).to(dt)
+    has_vis = d["support"] is not None and d["mask_vis"].any()
+    has_txt = bool(d["mask_txt"].any())
+    sup = torch.from_numpy(d["support"]).to(dev).to(dt) if has_vis else None
+    kp = torch.from_numpy(np.nan_to_num(d["kpts"])).to(dev)
+    mv = torch.from_numpy(d["mask_vis"]).to(dev)
+    mt = torch.from_numpy(d["mask_txt"]).to(dev)
+    kt = torch.from_numpy(np.nan_to_num(d["kern_txt"])).to(dev).to(dt)
+    protos = torch.zeros((B, R, C), dtype=dt, device=dev)
+    heat = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.float32, device=dev)
+    dec = (torch.empty((B, R), dtype=torch.int32, device=dev),
+           torch.empty((B, R, 2), dtype=torch.float32, device=dev),
+           torch.empty((B, R), dtype=torch.float32, device=dev))
+    vkp = lambda: gkd.vkp_pool(sup, kp, mv, d["stride"], d["sigma"], out=protos)
+    call = lambda: gkd.kernel_heatmap(q, protos if has_vis else None, mv if has_vis else None,
+                                      kt if has_txt else None, mt if has_txt else None,
+                                      out=heat, out_decode=dec)
+
+    def step():
+        if has_vis:
+            vkp()
+        call()
+    for _ in range(5):
+        step()
+    warm = timed_calls(torch, call, n)
+    res = {"workload": f"{name}: B={B}, C={C} {d['dtype']}, {H}x{W} -> {4 * H}x{4 * W}, "
+                       f"rows padded to {R}, {rows} valid",
+           "heatmaps": rows, "alg_bytes": heat_bytes,
+           "call_ms_warm": stats(warm),
+           "gbps_warm": round(heat_bytes / (np.median(warm) * 1e-3) / 1e9, 1),
+           "hbm_frac_warm": round(heat_bytes / (np.median(warm) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "heatmaps_per_s_call": round(rows / (np.median(warm) * 1e-3), 1)}
+    if flush is not None:
+        cold = timed_calls(torch, call, n, flush)
+        res["call_ms_cold"] = stats(cold)
+        res["gbps_cold"] = round(heat_bytes / (np.median(cold) * 1e-3) / 1e9, 1)
+        res["hbm_frac_cold"] = round(heat_bytes / (np.median(cold) * 1e-3) / 1e9
+                                     / HBM_PEAK_GBS, 4)
+    if has_vis:
+        vw = timed_calls(torch, vkp, n)
+        res["vkp"] = {"alg_bytes": vkp_bytes, "ms_warm": stats(vw),
+                      "hbm_frac_warm": round(vkp_bytes / (np.median(vw) * 1e-3) / 1e9
+                                             / HBM_PEAK_GBS, 4)}
+        if flush is not None:
+            vc = timed_calls(torch, vkp, n, flush)
+            res["vkp"]["ms_cold"] = stats(vc)
+            res["vkp"]["hbm_frac_cold"] = round(vkp_bytes / (np.median(vc) * 1e-3) / 1e9
+                                                / HBM_PEAK_GBS, 4)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / n
+    res["step_ms"] = round(ms_step, 4)
+    res["heatmaps_per_s_step"] = round(rows / (ms_step * 1e-3), 1)
+    return res
+
+
+def oracle_timing(names=("tiny_visual", "text_f32", "dual_bf16", "longtail_bf16",
+                         "highres_bf16"), budget_s=4.0):
+    """The oracle chain (VKP, then the heatmaps) timed on the first crops of
+    each workload, all host threads, until about budget_s seconds each."""
+    import gkdsynth
+    import oracle
+    out = {"cores": oracle.max_threads(), "cpu_model": host_cpu_model()}
+    for name in names:
+        d = gkdsynth.make(name)
+        crops = rows = 0
+        t0 = time.perf_counter()
+        while crops < d["B"] and time.perf_counter() - t0 < budget_s:
+            sl = slice(crops, crops + 1)
+            mv, mt = d["mask_vis"][sl], d["mask_txt"][sl]
+            kv = (oracle.vkp_pool(d["support"][sl], d["kpts"][sl], mv, d["stride"], d["sigma"],
+                                  dtype=d["dtype"]) if mv.any() else None)
+            oracle.kernel_heatmap(d["query"][sl], kv, mv if mv.any() else None,
+                                  d["kern_txt"][sl] if mt.any() else None,
+                                  mt if mt.any() else None)
+            rows += int(((mv | mt) > 0).sum())
+            crops += 1
+        sec = time.perf_counter() - t0
+        out[name] = {"crops": crops, "of": d["B"], "heatmaps": rows, "seconds": round(sec, 3),
+                     "heatmaps_per_s": round(rows / sec, 2), "crops_per_s": round(crops / sec, 3)}
+    return out
 
 
 def latency_mode(torch, gkd, n=50):
@@ -464,8 +667,12 @@ def main():
     ap.add_argument("--copy-only", action="store_true")
     ap.add_argument("--roi-only", action="store_true",
                     help="time only the ROI stage and print its JSON (profiling runs)")
+    ap.add_argument("--kg-only", action="store_true",
+                    help="time only the kernel-generation transformer (profiling runs)")
     ap.add_argument("--no-modes", action="store_true",
-                    help="skip the bf16-heatmap and keypoints-only passes (profiling runs)")
+                    help="headline only: skip the secondary modes and configs (profiling runs)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache (1 GiB write between calls) timings")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -508,21 +715,18 @@ def main():
     has_txt = bool(d["mask_txt"].any())
     torch.cuda.synchronize()
 
+    if args.kg_only:
+        if not (has_vis and has_txt and q.dtype == torch.bfloat16):
+            sys.exit("--kg-only needs a bf16 workload with both prompt modalities")
+        gkd.vkp_pool(sup, kp, mv, d["stride"], d["sigma"], out=protos)
+        d["support_t"] = sup
+        print(json.dumps(kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows,
+                                 n=max(3, args.steps))), flush=True)
+        return
+
     heat16 = None  # bfloat16 heatmaps (GKD_HEATMAP_BF16), for the secondary mode
 
-    def step(ev=None, ev_vkp=None, bf16_heat=False, kp_only=False):
-        # ev: events around the heatmap call (the roofline's kernel);
-        # ev_vkp: around the VKP launch (a separate, untimed pass);
-        # bf16_heat / kp_only: the same step with bfloat16 heatmaps, or with
-        # the keypoints only (separate passes)
-        if ev_vkp is not None:
-            ev_vkp[0].record()
-        if has_vis:
-            gkd.vkp_pool(sup, kp, mv, d["stride"], d["sigma"], out=protos)
-        if ev_vkp is not None:
-            ev_vkp[1].record()
-        if ev is not None:
-            ev[0].record()
+    def heatmap_call(bf16_heat=False, kp_only=False):
         if kp_only:
             gkd.kernel_heatmap(q, protos if has_vis else None, mv if has_vis else None,
                                kt if has_txt else None, mt if has_txt else None,
@@ -532,6 +736,19 @@ def main():
                                kt if has_txt else None, mt if has_txt else None,
                                out=heat16 if bf16_heat else heat, out_decode=(idx, xy, score),
                                heat_dtype=torch.bfloat16 if bf16_heat else torch.float32)
+
+    def vkp_call():
+        if has_vis:
+            gkd.vkp_pool(sup, kp, mv, d["stride"], d["sigma"], out=protos)
+
+    def step(ev=None, bf16_heat=False, kp_only=False):
+        # ev: events around the heatmap call (the roofline's kernel);
+        # bf16_heat / kp_only: the same step with bfloat16 heatmaps, or with
+        # the keypoints only (separate passes)
+        vkp_call()
+        if ev is not None:
+            ev[0].record()
+        heatmap_call(bf16_heat, kp_only)
         if ev is not None:
             ev[1].record()
 
@@ -554,16 +771,34 @@ def main():
     ms_step = wall * 1e3 / args.steps
     hm_all = np.array([e[0].elapsed_time(e[1]) for e in evs])
     hm_ms = float(hm_all.mean())
-    # the VKP launch duration, from a separate pass of a few steps
-    evv = [[TimingEvent(torch) for _ in range(2)] for _ in range(5)]
-    for k in range(5):
-        step(ev_vkp=evv[k])
-    torch.cuda.synchronize()
-    vkp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evv]))
+    # the VKP launch duration, from a separate pass (event-timed, back to back)
+    vkp_all = timed_calls(torch, vkp_call, 20) if has_vis else np.zeros(1)
+    vkp_ms = float(vkp_all.mean())
+    # keep the outputs of the timed steps for the parity check
+    heat_keep = heat.cpu().numpy() if not args.no_cpu_baseline else None
+    idx_keep = idx.cpu().numpy()
+    protos_keep = protos.float().cpu().numpy() if has_vis else None
+
+    cold = None
+    flush = None
+    if not args.no_cold:
+        log("[bench] cold-cache calls")
+        flush = make_flush(torch)
+        hm_cold = timed_calls(torch, lambda: heatmap_call(), 50, flush)
+        cold = {"note": "the heatmap call alone with a 1 GiB buffer write between calls "
+                        "(no input byte left in L2 or the memory-side cache), 50 calls",
+                "call_ms": stats(hm_cold),
+                "hbm_frac": round(heat_bytes / (np.median(hm_cold) * 1e-3) / 1e9
+                                  / HBM_PEAK_GBS, 4)}
+        if has_vis:
+            vkp_cold = timed_calls(torch, vkp_call, 50, flush)
+            cold["vkp_ms"] = stats(vkp_cold)
+            cold["vkp_hbm_frac"] = round(vkp_bytes / (np.median(vkp_cold) * 1e-3) / 1e9
+                                         / HBM_PEAK_GBS, 4)
 
     modes = None
     if not args.no_modes:
-        # secondary mode, outside the headline: the same steps with bfloat16
+        # secondary modes, outside the headline: the same steps with bfloat16
         # heatmaps (half the bytes of the dominant output stream)
         heat16 = torch.empty((B, R, 4 * H, 4 * W), dtype=torch.bfloat16, device=dev)
         n16 = max(20, args.steps // 4)
@@ -593,6 +828,11 @@ def main():
         mskp = (time.perf_counter() - t0) * 1e3 / n16
         hmkp = float(np.mean([e[0].elapsed_time(e[1]) for e in evk]))
         kp_bytes = heat_bytes - rows * 16 * H * W * 4  # no heatmap bytes
+        log("[bench] other configurations")
+        cfgs = {}
+        for name in ("dual_bf16", "highres_bf16"):
+            if name != args.workload:
+                cfgs[name] = config_mode(torch, gkd, name, flush=flush)
         log("[bench] ROI stage")
         roi = roi_stage(torch, gkd, with_cpu=not args.no_cpu_baseline)
         log("[bench] dense long-tail batch")
@@ -609,6 +849,7 @@ def main():
                            kt if has_txt else None, mt if has_txt else None, heat,
                            (idx, xy, score), heat_bytes, rows)
         modes = {
+            "configs": cfgs,
             "kg_transformer": kgr,
             "latency_small": lat,
             "query_tokens": toks,
@@ -637,21 +878,24 @@ def main():
 
     cpu = None
     parity = None
+    oracle_cfgs = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on a bounded sample")
         import oracle
-        rate, sample, ora_heat = cpu_baseline(d)
+        rate, sample, ora_heat, ora_protos = cpu_baseline(d, protos_keep)
         cpu = {"value": round(rate, 3), "unit": "heatmaps/s",
                "cores": oracle.max_threads(), "kind": "oracle",
+               "cpu_model": host_cpu_model(),
                "sample": (f"first {sample['crops']} crops of the {args.workload} batch "
-                          f"({sample['rows']} heatmaps, VKP + heatmap chain, "
-                          f"{sample['seconds']:.1f} s)"),
+                          f"({sample['rows']} heatmaps; VKP {sample['vkp_s']:.1f} s + "
+                          f"heatmaps {sample['heat_s']:.1f} s)"),
                "one_crop_one_thread_s": round(sample["one_crop_1thread_s"], 3),
                "one_crop_rows": sample["one_crop_rows"]}
-        # parity of the timed outputs on the sampled crops (the oracle chain
-        # uses its own prototypes, so this is an end-to-end check)
-        hg = heat.cpu().numpy()
-        parity = check_parity(d, hg, (idx.cpu().numpy(),), ora_heat)
+        # parity of the timed outputs on the sampled crops
+        parity = check_parity(d, heat_keep, idx_keep, ora_heat, protos_keep, ora_protos)
+        if not args.no_modes:
+            log("[bench] oracle timing per configuration")
+            oracle_cfgs = oracle_timing()
 
     value = rows / (ms_step * 1e-3)
     out = {
@@ -677,6 +921,8 @@ def main():
         "cpu_baseline": cpu,
         "keypoints_per_s": round(value, 1),
         "crops_per_s": round(B / (ms_step * 1e-3), 1),
+        "timing": "steady state: steps back to back, each VKP behind the previous "
+                  "call's write stream; kernel times are fence-free events around each call",
         "kernels": {
             "gkd_kernel_heatmap": {"ms": round(hm_ms, 4), "alg_bytes": heat_bytes,
                                    "gbps": round(achieved, 1),
@@ -684,12 +930,16 @@ def main():
                                                       np.percentile(hm_all, [10, 50, 90])]},
             "gkd_vkp_pool": {"ms": round(vkp_ms, 4), "alg_bytes": vkp_bytes,
                              "gbps": round(vkp_bytes / (vkp_ms * 1e-3) / 1e9, 1)
-                             if vkp_ms > 0 else None},
+                             if vkp_ms > 0 else None,
+                             "ms_p10_p50_p90": [round(float(x), 4) for x in
+                                                np.percentile(vkp_all, [10, 50, 90])]},
         },
+        "cold": cold,
         "step_hbm_frac": round((heat_bytes + vkp_bytes) / (ms_step * 1e-3) / 1e9
                                / HBM_PEAK_GBS, 4),
         "copy_gbps_measured": round(copy_gbs, 1),
         "modes": modes,
+        "oracle_per_config": oracle_cfgs,
         "parity": parity,
     }
     print(json.dumps(out), flush=True)

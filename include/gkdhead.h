@@ -39,6 +39,12 @@
  *   - B == 0 or R == 0 is an empty batch: GKD_OK, nothing launched.
  *   - Every element count (e.g. B*R*4H*4W) must be below 2^31.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified results.
+ *   - Kernel-row norms are taken in float32, so every kernel row of
+ *     gkd_kernel_heatmap must have ||k||_2 < 2^64 (about 1.8e19; bfloat16
+ *     rows reach it only with elements above about 5.8e17). Larger rows
+ *     give unspecified results (their squared norm overflows to infinity
+ *     and the row's map comes out zero). Rows with ||k||_2 below 1e-12,
+ *     zero rows included, are scaled by 1e12 (the clamp of the norm).
  *   - `flags` must be 0 (else GKD_ERR_UNSUPPORTED), except for the
  *     heatmap output format, upsample grid and query layout flags of
  *     gkd_kernel_heatmap (GKD_HEATMAP_BF16, GKD_UPSAMPLE_CORNERS,
@@ -85,8 +91,10 @@ extern "C" {
  * H*W % 16 == 0 (H*W <= 576 for keypoints only), else
  * GKD_ERR_UNSUPPORTED. The results equal, bit for bit, those of the same
  * call on the [B, C, H, W] layout. gkd_vkp_pool takes the same flag for its
- * support map (any dtype and shape; it then runs the general VKP kernel,
- * whose results agree with the fast one's within rounding). */
+ * support map, for any dtype and shape, and its prototypes equal those of
+ * the same call on the [B, C, H, W] layout bit for bit: bfloat16 maps with
+ * H, W <= 32, W % 8 == 0, C % 16 == 0 and R <= 256 take the fast VKP kernel
+ * in either layout, all other shapes and float32 the general one. */
 #define GKD_QUERY_TOKENS 0x8u
 #define GKD_QUERY_SKIP(n) (((uint32_t)(n) & 255u) << 8)
 

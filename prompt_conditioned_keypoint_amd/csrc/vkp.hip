@@ -235,7 +235,6 @@ __global__ __launch_bounds__(kVThreads) void vkp_kernel(VkParams p) {
 constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;  // 512
 constexpr int kFRows = 80;                  // valid rows per item
-constexpr int kFMaxMT = kFRows / 16;
 constexpr int kFMaxHW = 32;                 // H, W <= 32 (one half wave per weight row)
 constexpr int kFCh = kFWaves * 16;          // channels per item
 constexpr int kFDepth = 4;                  // image rows loaded ahead per wave

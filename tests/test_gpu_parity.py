@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import gkdsynth
-from parity_util import (check_decode, check_heatmaps, check_protos, dev_tensor,
-                         feat_dtype, floors_of)
+from parity_util import (check_decode, check_heatmaps, check_heatmaps_internal, check_protos,
+                         dev_tensor, feat_dtype, floors_of, internal_bounds)
 
 pytestmark = pytest.mark.gpu
 
@@ -103,8 +103,8 @@ def sample_crops(d, n):
     return sorted(picks)
 
 
-CASES = [("tiny_visual", {}, None), ("text_f32", {}, None), ("dual_bf16", {}, 6),
-         ("longtail_bf16", {}, 8), ("highres_bf16", {}, 2), ("longtail_dense", {}, 3)]
+CASES = [("tiny_visual", {}, None), ("text_f32", {}, None), ("dual_bf16", {}, 8),
+         ("longtail_bf16", {}, 12), ("highres_bf16", {}, 6), ("longtail_dense", {}, 8)]
 
 
 @pytest.mark.parametrize("name,kw,nsample", CASES, ids=[c[0] for c in CASES])
@@ -147,6 +147,9 @@ def test_kernel_heatmap_parity(gkd, ora, name, kw, nsample):
     oh = oracle_heat(ora, d, protos, crops)
     fl = floors_of(d["query"][crops])
     check_heatmaps(g[crops], oh, valid[crops], d["dtype"], fl)
+    if d["dtype"] == "bf16":
+        # the same bf16 values on both sides: float32-evaluation bound too
+        check_heatmaps_internal(g[crops], oh, valid[crops], internal_bounds(d["query"][crops]))
     n_exact, n_near = check_decode((idx.cpu().numpy()[crops], xy.cpu().numpy()[crops],
                                     score.cpu().numpy()[crops]), oh, valid[crops],
                                    d["dtype"], floors=fl)
@@ -280,6 +283,8 @@ def test_ragged_shapes(gkd, ora, dtype, shape):
     valid = ((mv | mt) > 0).astype(np.uint8)
     fl = floors_of(q)
     check_heatmaps(heat.cpu().numpy(), oh, valid, dtype, fl)
+    if dtype == "bf16":
+        check_heatmaps_internal(heat.cpu().numpy(), oh, valid, internal_bounds(q))
     check_decode((idx.cpu().numpy(), xy.cpu().numpy(), score.cpu().numpy()), oh, valid, dtype,
                  floors=fl)
     assert np.all(heat.view(torch.int32).cpu().numpy()[valid == 0] == NAN_BITS)

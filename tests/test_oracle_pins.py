@@ -459,3 +459,40 @@ def test_vkp_rounds_to_dtype(oracle_mod):
                                   oracle_mod.round_bf16(d))
     np.testing.assert_array_equal(oracle_mod.vkp_pool(S, kp, one, dtype="f32"),
                                   d.astype(np.float32).astype(np.float64))
+
+
+def test_round_bf16_subnormal_and_overflow_branches(oracle_mod):
+    """The two range branches of the oracle's bfloat16 rounding, against
+    torch's float32 -> bfloat16 cast (round to nearest even on the bit
+    pattern, which covers subnormals and the overflow to infinity):
+      * float32 subnormals (|v| < 2^-126, fixed quantum 2^-133 in bf16),
+        including halfway cases and the round-up into the smallest normal;
+      * the top binade, up to and past the largest finite bfloat16
+        (2 - 2^-7) 2^127: halfway to 2^128 rounds to even, i.e. to
+        infinity, and anything above it too."""
+    rng = np.random.default_rng(41)
+    sub_bits = rng.integers(1, 1 << 23, size=4000, dtype=np.uint32)
+    sub = sub_bits.view(np.float32)
+    sign = np.where(rng.random(4000) < 0.5, -1.0, 1.0).astype(np.float32)
+    sub = sub * sign
+    # halfway between bf16 subnormals (low 16 bits 0x8000), and the largest
+    # float32 subnormals (round up to 2^-126)
+    halves = (np.arange(1, 128, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    top_sub = np.array([0x007FFFFF, 0x007F8000, 0x007F7FFF], np.uint32).view(np.float32)
+    top_bits = rng.integers(0x7F000000, 0x7F800000, size=4000, dtype=np.uint32)
+    big = top_bits.view(np.float32)
+    edge = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0x7F7FFFFF, 0x7F7F0000,
+                     0x7F7E8000], np.uint32).view(np.float32)
+    x32 = np.concatenate([sub, halves, -halves, top_sub, big, -big, edge, -edge])
+    ref = torch.from_numpy(x32.copy()).to(torch.bfloat16).double().numpy()
+    got = oracle_mod.round_bf16(x32.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    assert np.isinf(got).sum() > 0 and (np.abs(got[np.isfinite(got)]) < 2.0 ** -126).sum() > 0
+    # doubles between float32 values: rounded once, from the double
+    q = 2.0 ** -133
+    assert oracle_mod.round_bf16(5.5 * q) == 6 * q            # tie to even (up)
+    assert oracle_mod.round_bf16(4.5 * q) == 4 * q            # tie to even (down)
+    assert oracle_mod.round_bf16(4.5 * q + 2.0 ** -160) == 5 * q
+    assert oracle_mod.round_bf16(255.5 * 2.0 ** 120 - 2.0 ** 80) == 255 * 2.0 ** 120
+    assert oracle_mod.round_bf16(255.5 * 2.0 ** 120) == np.inf
+    assert oracle_mod.round_bf16(-1e300) == -np.inf
