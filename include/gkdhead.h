@@ -59,7 +59,8 @@
  * GKD_COORDS_CORNERS; version 5 adds GKD_UPSAMPLE_CORNERS; version 6 adds
  * GKD_QUERY_TOKENS; version 7 accepts it in gkd_vkp_pool for the support
  * map; version 8 adds the kernel-generation transformer
- * (gkd_kg_workspace_size, gkd_kg_transformer).
+ * (gkd_kg_workspace_size, gkd_kg_transformer); version 9 adds
+ * gkd_kg_transformer_noalloc.
  */
 #ifndef GKDHEAD_H
 #define GKDHEAD_H
@@ -71,7 +72,7 @@
 extern "C" {
 #endif
 
-#define GKD_ABI_VERSION 8
+#define GKD_ABI_VERSION 9
 
 /* gkd_kernel_heatmap flag: store the heatmaps as bfloat16 instead of float32
  * (half the bytes of the dominant output stream). */
@@ -341,6 +342,35 @@ GKD_API gkd_status gkd_kg_transformer(const void *kern_vis, const uint8_t *mask_
                                       gkd_dtype dtype, uint32_t flags, void *out,
                                       void *workspace, size_t workspace_bytes,
                                       hipStream_t stream);
+
+/*
+ * gkd_kg_transformer_noalloc - gkd_kg_transformer for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. It takes no workspace argument:
+ * the workspace is an array of GKD_KG_STATIC_WORKSPACE_BYTES inside the
+ * library's device code, one per GPU, placed when the library is loaded
+ * on that GPU and held until the process ends. The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a GPU
+ * looks up that GPU's copy of the array (hipGetSymbolAddress), with the
+ * current device being the one `stream` runs on.
+ *   - Arguments, results and errors are those of gkd_kg_transformer,
+ *     which this call equals bit for bit; a shape whose
+ *     gkd_kg_workspace_size() exceeds GKD_KG_STATIC_WORKSPACE_BYTES is
+ *     rejected with GKD_ERR_VALUE before anything is launched (at C = 1024,
+ *     H = W = 24, R = 80, d_ff = 1024: up to 10 crops per call, 12 with
+ *     GKD_QUERY_TOKENS).
+ *   - All calls on one GPU share its array and nothing in it needs to
+ *     start at zero; two calls that overlap in time on one GPU (different
+ *     streams, or host threads without stream ordering) race on it and
+ *     give undefined results.
+ */
+#define GKD_KG_STATIC_WORKSPACE_BYTES (64u << 20)
+GKD_API gkd_status gkd_kg_transformer_noalloc(const void *kern_vis, const uint8_t *mask_vis,
+                                              const void *kern_txt, const uint8_t *mask_txt,
+                                              const void *query, int B, int C, int H, int W,
+                                              int R, const void *weights, int n_blocks,
+                                              int d_ff, gkd_dtype dtype, uint32_t flags,
+                                              void *out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

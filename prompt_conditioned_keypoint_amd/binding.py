@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgkdhead.so")
 
 GKD_DTYPE_F32, GKD_DTYPE_BF16 = 0, 1
-GKD_ABI_VERSION = 8          # include/gkdhead.h
+GKD_ABI_VERSION = 9          # include/gkdhead.h
+GKD_KG_STATIC_WORKSPACE_BYTES = 64 << 20  # the no-allocation KG call's static workspace
 GKD_HEATMAP_BF16 = 0x1       # gkd_kernel_heatmap flag: bfloat16 heatmaps
 GKD_UPSAMPLE_CORNERS = 0x2   # gkd_kernel_heatmap flag: align_corners=True upsample
 GKD_COORDS_CORNERS = 0x4     # decode flag: corner-aligned -1..1 coordinates
@@ -69,6 +70,9 @@ def load():
     lib.gkd_kg_transformer.restype = _I
     lib.gkd_kg_transformer.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _I,
                                        _U32, _P, _P, ctypes.c_size_t, _P]
+    lib.gkd_kg_transformer_noalloc.restype = _I
+    lib.gkd_kg_transformer_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I,
+                                               _I, _I, _U32, _P, _P]
     if lib.gkd_abi_version() != GKD_ABI_VERSION:
         raise ImportError("libgkdhead ABI version mismatch")
     _lib = lib
@@ -310,7 +314,9 @@ def kg_transformer(query: torch.Tensor, weights: torch.Tensor, kern_vis=None, ma
     query [B,C,H,W] bf16, or with token_hw=(H, W) the token sequence
     [B, token_skip + H*W, C]; weights: the flat bf16 array. workspace: a
     uint8 CUDA tensor of at least kg_workspace_size() bytes (allocated here
-    when None)."""
+    when None), or "static" for gkd_kg_transformer_noalloc (the library's
+    static workspace of GKD_KG_STATIC_WORKSPACE_BYTES per GPU; nothing is
+    allocated by the call, `out` included when it is given)."""
     lib = load()
     if token_hw is None:
         _dev(query, "query", torch.bfloat16, 4)
@@ -340,13 +346,17 @@ def kg_transformer(query: torch.Tensor, weights: torch.Tensor, kern_vis=None, ma
     _dev(out, "out", torch.bfloat16, 4)
     if out.shape != (2, B, R, C):
         raise ValueError("out must be [2,B,R,C]")
+    args = (_ptr(kern_vis) if mask_vis is not None else None, _ptr(mask_vis),
+            _ptr(kern_txt) if mask_txt is not None else None, _ptr(mask_txt), _ptr(query),
+            B, C, H, W, R, _ptr(weights), n_blocks, d_ff, 1, flags, _ptr(out))
+    if workspace == "static":
+        # no workspace argument: the library's own static device array
+        _check(lib.gkd_kg_transformer_noalloc(*args, _stream(query.device)))
+        return out
     need = int(lib.gkd_kg_workspace_size(B, C, H, W, R, d_ff, flags))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=query.device)
     _dev(workspace, "workspace", torch.uint8, 1)
-    _check(lib.gkd_kg_transformer(
-        _ptr(kern_vis) if mask_vis is not None else None, _ptr(mask_vis),
-        _ptr(kern_txt) if mask_txt is not None else None, _ptr(mask_txt), _ptr(query),
-        B, C, H, W, R, _ptr(weights), n_blocks, d_ff, 1, flags, _ptr(out), _ptr(workspace),
-        workspace.numel(), _stream(query.device)))
+    _check(lib.gkd_kg_transformer(*args, _ptr(workspace), workspace.numel(),
+                                  _stream(query.device)))
     return out

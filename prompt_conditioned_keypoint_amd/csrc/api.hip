@@ -7,7 +7,9 @@
 #include "launch.hpp"
 #include "kg_launch.hpp"
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -276,46 +278,52 @@ size_t gkd_kg_workspace_size(int B, int C, int H, int W, int R, int d_ff, uint32
   return gkd::kg_workspace_bytes(B, C, H, W, R, d_ff, (flags & GKD_QUERY_TOKENS) != 0);
 }
 
-gkd_status gkd_kg_transformer(const void* kern_vis, const uint8_t* mask_vis, const void* kern_txt,
-                              const uint8_t* mask_txt, const void* query, int B, int C, int H,
-                              int W, int R, const void* weights, int n_blocks, int d_ff,
-                              gkd_dtype dtype, uint32_t flags, void* out, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by gkd_kg_transformer and its no-allocation variant:
+// everything but the workspace; fills `a` (workspace excluded) and the
+// workspace size the call needs. On GKD_OK with B == 0 or R == 0 the call
+// is empty (*empty set).
+gkd_status kg_check(const char* fn, const void* kern_vis, const uint8_t* mask_vis,
+                    const void* kern_txt, const uint8_t* mask_txt, const void* query, int B,
+                    int C, int H, int W, int R, const void* weights, int n_blocks, int d_ff,
+                    gkd_dtype dtype, uint32_t flags, void* out, gkd::KgArgs& a, size_t& need,
+                    bool& empty) {
   const bool tokens = (flags & GKD_QUERY_TOKENS) != 0;
   const int skip = (int)((flags >> 8) & 255u);
+  empty = false;
   if ((flags & ~(uint32_t)(GKD_QUERY_TOKENS | GKD_QUERY_SKIP(255))) != 0 || (!tokens && skip != 0))
-    return fail(GKD_ERR_UNSUPPORTED, "gkd_kg_transformer: unknown flags 0x%x", (unsigned)flags);
+    return fail(GKD_ERR_UNSUPPORTED, "%s: unknown flags 0x%x", fn, (unsigned)flags);
   if (dtype != GKD_DTYPE_F32 && dtype != GKD_DTYPE_BF16)
-    return fail(GKD_ERR_DTYPE, "gkd_kg_transformer: unknown dtype %d", (int)dtype);
+    return fail(GKD_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)dtype);
   if (dtype != GKD_DTYPE_BF16)
-    return fail(GKD_ERR_UNSUPPORTED, "gkd_kg_transformer: needs bfloat16 operands");
+    return fail(GKD_ERR_UNSUPPORTED, "%s: needs bfloat16 operands", fn);
   if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1 || d_ff < 1 || n_blocks < 1)
-    return fail(GKD_ERR_SHAPE, "gkd_kg_transformer: bad shape B=%d C=%d H=%d W=%d R=%d d_ff=%d "
-                "n_blocks=%d", B, C, H, W, R, d_ff, n_blocks);
+    return fail(GKD_ERR_SHAPE, "%s: bad shape B=%d C=%d H=%d W=%d R=%d d_ff=%d "
+                "n_blocks=%d", fn, B, C, H, W, R, d_ff, n_blocks);
   if (C % 64 != 0 || d_ff % 64 != 0 || n_blocks > 64 || 2LL * R > 576 || (long long)H * W > 576)
-    return fail(GKD_ERR_UNSUPPORTED, "gkd_kg_transformer: needs C %% 64 == 0, d_ff %% 64 == 0, "
-                "n_blocks <= 64, 2R <= 576 and H*W <= 576");
+    return fail(GKD_ERR_UNSUPPORTED, "%s: needs C %% 64 == 0, d_ff %% 64 == 0, "
+                "n_blocks <= 64, 2R <= 576 and H*W <= 576", fn);
   const long long HW = (long long)H * W, M = 2LL * B * R;
   if (M * (C > d_ff ? C : d_ff) > kMaxElems || B * (HW + skip) * C > kMaxElems ||
       (long long)C * C * 8 + 2LL * C * d_ff > kMaxElems / n_blocks)
-    return fail(GKD_ERR_SHAPE, "gkd_kg_transformer: an element count reaches 2^31");
-  if (B == 0 || R == 0) return ok();
-  if (!query || !weights || !out || !workspace)
-    return fail(GKD_ERR_NULL, "gkd_kg_transformer: NULL pointer argument");
+    return fail(GKD_ERR_SHAPE, "%s: an element count reaches 2^31", fn);
+  need = gkd::kg_workspace_bytes(B, C, H, W, R, d_ff, tokens);
+  if (B == 0 || R == 0) {
+    empty = true;
+    return ok();
+  }
+  if (!query || !weights || !out)
+    return fail(GKD_ERR_NULL, "%s: NULL pointer argument", fn);
   if (!mask_vis && !mask_txt)
-    return fail(GKD_ERR_NULL, "gkd_kg_transformer: give mask_vis, mask_txt or both");
+    return fail(GKD_ERR_NULL, "%s: give mask_vis, mask_txt or both", fn);
   if ((mask_vis && !kern_vis) || (mask_txt && !kern_txt))
-    return fail(GKD_ERR_NULL, "gkd_kg_transformer: a mask without its prototypes");
+    return fail(GKD_ERR_NULL, "%s: a mask without its prototypes", fn);
   if (!aligned16(query) || !aligned16(weights) || !aligned16(out) ||
-      (mask_vis && !aligned16(kern_vis)) || (mask_txt && !aligned16(kern_txt)) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(GKD_ERR_ALIGN, "gkd_kg_transformer: arrays need 16-byte alignment, the "
-                "workspace 256-byte");
-  const size_t need = gkd::kg_workspace_bytes(B, C, H, W, R, d_ff, tokens);
-  if (workspace_bytes < need)
-    return fail(GKD_ERR_VALUE, "gkd_kg_transformer: workspace of %zu bytes, needs %zu",
-                workspace_bytes, need);
-  gkd::KgArgs a;
+      (mask_vis && !aligned16(kern_vis)) || (mask_txt && !aligned16(kern_txt)))
+    return fail(GKD_ERR_ALIGN, "%s: arrays need 16-byte alignment", fn);
   a.vis = mask_vis ? kern_vis : nullptr;
   a.mv = mask_vis;
   a.txt = mask_txt ? kern_txt : nullptr;
@@ -332,8 +340,92 @@ gkd_status gkd_kg_transformer(const void* kern_vis, const uint8_t* mask_vis, con
   a.n_blocks = n_blocks;
   a.d_ff = d_ff;
   a.out = out;
+  a.ws = nullptr;
+  return ok();
+}
+
+// The no-allocation variant's workspace: one array per GPU, in the
+// library's device code object (placed on each GPU when the library loads
+// there, held until the process ends). Its host-side name is not a device
+// address: kernels get the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in g_scratch_ptr.
+constexpr size_t kKgStaticBytes = (size_t)GKD_KG_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kKgStaticBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// This device's address of `scratch` (the current device), or null with
+// *err set.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+gkd_status gkd_kg_transformer(const void* kern_vis, const uint8_t* mask_vis, const void* kern_txt,
+                              const uint8_t* mask_txt, const void* query, int B, int C, int H,
+                              int W, int R, const void* weights, int n_blocks, int d_ff,
+                              gkd_dtype dtype, uint32_t flags, void* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  gkd::KgArgs a;
+  size_t need = 0;
+  bool empty = false;
+  const gkd_status st = kg_check("gkd_kg_transformer", kern_vis, mask_vis, kern_txt, mask_txt,
+                                 query, B, C, H, W, R, weights, n_blocks, d_ff, dtype, flags, out,
+                                 a, need, empty);
+  if (st != GKD_OK || empty) return st;
+  if (!workspace) return fail(GKD_ERR_NULL, "gkd_kg_transformer: NULL workspace");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(GKD_ERR_ALIGN, "gkd_kg_transformer: the workspace needs 256-byte alignment");
+  if (workspace_bytes < need)
+    return fail(GKD_ERR_VALUE, "gkd_kg_transformer: workspace of %zu bytes, needs %zu",
+                workspace_bytes, need);
   a.ws = workspace;
   return hip_status(gkd::launch_kg(a, stream), "gkd_kg_transformer");
+}
+
+gkd_status gkd_kg_transformer_noalloc(const void* kern_vis, const uint8_t* mask_vis,
+                                      const void* kern_txt, const uint8_t* mask_txt,
+                                      const void* query, int B, int C, int H, int W, int R,
+                                      const void* weights, int n_blocks, int d_ff,
+                                      gkd_dtype dtype, uint32_t flags, void* out,
+                                      hipStream_t stream) {
+  gkd::KgArgs a;
+  size_t need = 0;
+  bool empty = false;
+  const gkd_status st = kg_check("gkd_kg_transformer_noalloc", kern_vis, mask_vis, kern_txt,
+                                 mask_txt, query, B, C, H, W, R, weights, n_blocks, d_ff, dtype,
+                                 flags, out, a, need, empty);
+  if (st != GKD_OK || empty) return st;
+  if (need > kKgStaticBytes)
+    return fail(GKD_ERR_VALUE, "gkd_kg_transformer_noalloc: this shape needs %zu bytes of "
+                "workspace, the static workspace holds %zu (GKD_KG_STATIC_WORKSPACE_BYTES); "
+                "use gkd_kg_transformer with a workspace of that size", need, kKgStaticBytes);
+  hipError_t e = hipSuccess;
+  void* ws = scratch_on_current_device(&e);
+  if (ws == nullptr) return hip_status(e, "gkd_kg_transformer_noalloc: static workspace");
+  a.ws = ws;
+  return hip_status(gkd::launch_kg(a, stream), "gkd_kg_transformer_noalloc");
 }
 
 }  // extern "C"

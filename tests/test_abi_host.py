@@ -47,13 +47,14 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"gkd_vkp_pool", "gkd_kernel_heatmap", "gkd_peak_decode", "gkd_roi_preprocess",
-            "gkd_roi_backproject", "gkd_kg_workspace_size", "gkd_kg_transformer"} <= set(names)
+            "gkd_roi_backproject", "gkd_kg_workspace_size", "gkd_kg_transformer",
+            "gkd_kg_transformer_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gkd_abi_version() == 8
+    assert lib.gkd_abi_version() == 9
     for code, name in enumerate(["GKD_OK", "GKD_ERR_NULL", "GKD_ERR_SHAPE",
                                  "GKD_ERR_DTYPE", "GKD_ERR_VALUE",
                                  "GKD_ERR_UNSUPPORTED", "GKD_ERR_HIP",
@@ -289,3 +290,39 @@ def test_kg_transformer_empty_batch_is_ok_and_workspace_grows(lib):
     tok = lib.gkd_kg_workspace_size(256, 1024, 24, 24, 80, 1024, 0x8)
     assert 0 < small < big and tok < big
     assert lib.gkd_kg_workspace_size(2, 32, 24, 24, 80, 1024, 0) == 0
+
+
+def kg_static(lib, vis=A, mv=A2, txt=None, mt=None, query=A3, B=2, C=128, H=24, W=24, R=80,
+              weights=A, nb=2, F=1024, dtype=1, flags=0, out=A2):
+    return lib.gkd_kg_transformer_noalloc(vis, mv, txt, mt, query, B, C, H, W, R, weights, nb,
+                                          F, dtype, flags, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=1), UNSUP),
+    (dict(dtype=0), UNSUP),
+    (dict(C=96), UNSUP),
+    (dict(B=-1), SHAPE),
+    (dict(query=None), NULL),
+    (dict(mv=None), NULL),
+    (dict(out=A2 + 8), ALIGN),
+    # beyond the static workspace: 11 crops at the model card's shape
+    (dict(B=11, C=1024), VALUE),
+    (dict(B=256, C=1024), VALUE),
+])
+def test_kg_transformer_noalloc_rejects(lib, kw, status):
+    assert kg_static(lib, **kw) == status
+    assert lib.gkd_last_error().decode() != ""
+
+
+def test_kg_transformer_noalloc_limit_matches_workspace_size(lib):
+    """The documented limit: 10 crops fit the static workspace at C = 1024,
+    24x24, R = 80, d_ff = 1024 (12 as tokens), 11 (13) do not; the empty
+    batch is fine."""
+    import prompt_conditioned_keypoint_amd.binding as b
+    cap = b.GKD_KG_STATIC_WORKSPACE_BYTES
+    assert lib.gkd_kg_workspace_size(10, 1024, 24, 24, 80, 1024, 0) <= cap
+    assert lib.gkd_kg_workspace_size(11, 1024, 24, 24, 80, 1024, 0) > cap
+    assert lib.gkd_kg_workspace_size(12, 1024, 24, 24, 80, 1024, 0x8) <= cap
+    assert lib.gkd_kg_workspace_size(13, 1024, 24, 24, 80, 1024, 0x8) > cap
+    assert kg_static(lib, B=0, query=None, out=None) == OK
