@@ -298,8 +298,8 @@ GKD_API gkd_status gkd_roi_backproject(const float *xy, const int32_t *boxes, in
  * cross-attention, d_ff = 1024, a mask token; paper summary, four-step
  * pipeline). Readings: the sequence of a crop is its 2R slots [visual rows
  * 0..R-1, text rows 0..R-1]; a slot whose row lacks that prompt holds the
- * mask token; self-attention keys are the slots of rows with any prompt (a
- * crop with none gets a zero attention output); cross-attention keys and
+ * mask token; self-attention keys are the slots of rows with any prompt;
+ * cross-attention keys and
  * values are the H*W query feature tokens; each block is post-norm,
  * x = LN1(x + SA(x)), x = LN2(x + CA(x, F)), x = LN3(x + W2 relu(W1 x + b1)
  * + b2), LayerNorm eps 1e-5; heads are 64 wide (C/64 heads), scores scaled
@@ -320,7 +320,14 @@ GKD_API gkd_status gkd_roi_backproject(const float *xy, const int32_t *boxes, in
  *                                    y = x W^T + b)
  *   out        [2,B,R,C] bf16 (out)  kernels: out[0] from the visual slots,
  *                                    out[1] from the text slots (the head's
- *                                    kern_vis and kern_txt as they stand)
+ *                                    kern_vis and kern_txt as they stand).
+ *                                    Rows with no prompt in either modality
+ *                                    are not written: they are no
+ *                                    self-attention keys, so they change no
+ *                                    other row, and the head reads no
+ *                                    kernel of a masked row. Only the
+ *                                    2 n_b slots of crop b's n_b prompted
+ *                                    rows are computed.
  *   workspace  device memory of at least gkd_kg_workspace_size() bytes,
  *              256-byte aligned, owned by the caller; its contents on entry
  *              do not matter and are left undefined. Calls that share a

@@ -10,6 +10,15 @@
 // heads are 64 wide. The kernels come out as [2, B, R, C]: plane 0 the
 // visual kernels, plane 1 the text kernels, as the head takes them.
 //
+// Only the slots of prompted rows are computed: a row without a prompt
+// is no self-attention key, so it changes no other slot's output, and the
+// head never reads its kernels. kg_compact_kernel lists the 2 n_b slots of
+// the n_b prompted rows of crop b (visual slots, then text slots) as
+// consecutive rows of a compact matrix starting at off[b]; every dense
+// layer and both attentions run over those rows only, and the last
+// LayerNorm scatters them to their [2, B, R, C] places (other rows are not
+// written).
+//
 // bfloat16 throughout for matrix operands (weights, prototypes, features,
 // and every activation that feeds a product), float32 for accumulation, the
 // residual stream, softmax and LayerNorm. Per block:
@@ -29,9 +38,6 @@ namespace {
 constexpr int kHd = 64;          // head width
 constexpr int kMaxKeys = 576;    // attention keys held in registers (36 tiles of 16)
 constexpr int kKeyTiles = kMaxKeys / 16;
-constexpr int kGT = 128;         // GEMM tile (M and N)
-constexpr int kGK = 64;          // GEMM K step
-constexpr int kGPitch = kGK + 8; // bf16 per LDS tile row (16-B aligned, skewed banks)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
@@ -47,7 +53,8 @@ __host__ __device__ __forceinline__ int rup32(int n) { return (n + 31) & ~31; }
 // token sequence with leading special tokens is read in place.
 // Epilogues: kOutBf16 (optionally ReLU); columns >= tsplit go to vt
 // transposed per head, vt[((b * nh + h) * 64 + d) * vt_ld + p] with
-// b = m / t_rows, p = m % t_rows; kOutResF32: float32 acc + bias + res.
+// b = m / t_rows, p = m % t_rows, or (vt null) row-major to out2;
+// kOutResF32: float32 acc + bias + res.
 // ---------------------------------------------------------------------------
 enum { kOutBf16 = 0, kOutBf16Relu = 1, kOutResF32 = 2 };
 
@@ -57,7 +64,8 @@ struct GemmParams {
   int a_rows, lda;
   const uint16_t* W;
   const uint16_t* bias;
-  int M, N, K;
+  int M, N, K;          // M: rows the grid covers
+  const int* m_dev;     // or null: the actual row count (<= M) is *m_dev
   int mode;
   uint16_t* out_bf;
   float* out_f;
@@ -66,137 +74,221 @@ struct GemmParams {
   int tsplit;
   uint16_t* vt;
   int t_rows, vt_ld, nh;
+  uint16_t* out2;  // with vt null: columns >= tsplit go here, row-major, ld2
+  int ld2;
 };
 
-__global__ __launch_bounds__(256) void kg_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kGT * kGPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kGT * kGPitch];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tiles_n = (p.N + kGT - 1) / kGT;
+typedef __attribute__((address_space(3))) void kg_lds_void;
+typedef __attribute__((address_space(1))) void kg_glb_void;
+
+// Workgroup tile 256 x BN, K step 64, 8 waves: BN = 256 as 2 x 4 wave tiles
+// of 128 x 64, BN = 128 as 4 x 2 wave tiles of 64 x 64 (MT x 4 MFMA tiles
+// of 16 x 16 per wave). Both operand tiles stream straight into LDS
+// (global_load_lds, 16 bytes a lane): row r of a tile is 128 bytes, eight
+// 16-byte chunks, and chunk c of row r is stored at chunk position
+// c ^ (r & 7), so the 16 rows an MFMA operand read touches fall in
+// different banks. Two stages: the loads of K step k + 1 are issued right
+// after the barrier of step k and land while step k computes.
+constexpr int kGM = 256, kGK = 64;
+
+template <int BN>
+__host__ __device__ constexpr size_t gemm_stage_bytes() {
+  return (size_t)(kGM + BN) * kGK * 2;
+}
+
+template <int BN>
+__global__ __launch_bounds__(512) void kg_gemm_kernel(GemmParams p) {
+  constexpr int WM = BN == 256 ? 128 : 64;  // wave tile rows
+  constexpr int MT = WM / 16;
+  constexpr int NT = 4;                     // wave tile columns: 64
+  constexpr int WN = BN / 64;               // waves across N
+  constexpr int A_BYTES = kGM * kGK * 2;
+  constexpr int STAGE = (kGM + BN) * kGK * 2;
+  constexpr int NA = kGM * 8 / 64 / 8;      // A loads per wave and step (16-B chunks / 64 lanes / 8 waves)
+  constexpr int NB = BN * 8 / 64 / 8;
+  extern __shared__ __attribute__((aligned(16))) unsigned char glds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_n = (p.N + BN - 1) / BN;
   const int total = gridDim.x;
   int lin = blockIdx.x;
   // Workgroups are dealt round-robin over the 8 XCDs; give each XCD a
   // contiguous run of tiles so the N-tiles of one A row band share an L2.
   if ((total & (kXcds - 1)) == 0) lin = (lin % kXcds) * (total / kXcds) + lin / kXcds;
-  const int m0 = (lin / tiles_n) * kGT, n0 = (lin % tiles_n) * kGT;
-
-  // Each thread moves 4 A and 4 W chunks of 16 B per K step:
-  // chunk c = tid + 256 i -> tile row c >> 3, 8-element column group c & 7.
-  const uint16_t* arow[4];
-  const uint16_t* wrow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, r = c >> 3, cg = (c & 7) * 8;
-    const int m = min(m0 + r, p.M - 1), n = min(n0 + r, p.N - 1);
-    arow[i] = p.A + (long long)(m / p.a_rows) * p.a_bstride + (long long)(m % p.a_rows) * p.lda + cg;
-    wrow[i] = p.W + (long long)n * p.K + cg;
+  const int m0 = (lin / tiles_n) * kGM, n0 = (lin % tiles_n) * BN;
+  if (p.m_dev != nullptr) {
+    const int mr = *p.m_dev;  // compact rows: tiles past them have nothing to do
+    if (m0 >= mr) return;
+    p.M = mr;
   }
-  u32x4 ra[4], rw[4];
-  auto load = [&](int k0) {
+
+  // per-lane element offsets of the chunks this lane loads (step 0)
+  uint32_t aoff[NA], woff[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + k0);
-      rw[i] = *reinterpret_cast<const u32x4*>(wrow[i] + k0);
-    }
-  };
-  auto stash = [&](int buf) {
+  for (int i = 0; i < NA; ++i) {
+    const int q = (wave + 8 * i) * 64 + lane, r = q >> 3, cs = (q & 7) ^ (r & 7);
+    const int m = min(m0 + r, p.M - 1);
+    aoff[i] = (uint32_t)((long long)(m / p.a_rows) * p.a_bstride + (long long)(m % p.a_rows) * p.lda +
+                         8 * cs);
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, off = (c >> 3) * kGPitch + (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(&sA[buf][off]) = ra[i];
-      *reinterpret_cast<u32x4*>(&sB[buf][off]) = rw[i];
-    }
+  for (int i = 0; i < NB; ++i) {
+    const int q = (wave + 8 * i) * 64 + lane, r = q >> 3, cs = (q & 7) ^ (r & 7);
+    const int n = min(n0 + r, p.N - 1);
+    woff[i] = (uint32_t)((long long)n * p.K + 8 * cs);
+  }
+  auto issue = [&](int stage, int k0) {
+    unsigned char* base = glds + (size_t)stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      __builtin_amdgcn_global_load_lds((kg_glb_void*)(p.A + aoff[i] + k0),
+                                       (kg_lds_void*)(base + (size_t)(wave + 8 * i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      __builtin_amdgcn_global_load_lds((kg_glb_void*)(p.W + woff[i] + k0),
+                                       (kg_lds_void*)(base + A_BYTES + (size_t)(wave + 8 * i) * 1024),
+                                       16, 0, 0);
   };
 
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  f32x4 acc[4][4];
+  const int wm0 = (wave / WN) * WM, wn0 = (wave % WN) * 64;
+  const int fr = lane & 15, g = lane >> 4;
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = p.K / kGK;
-  load(0);
-  stash(0);
-  __syncthreads();
+  issue(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kGK);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);  // vmcnt(0): this step's loads landed
+    __syncthreads();                              // everyone's; the other stage is free
+    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kGK);
+    const unsigned char* sa = glds + (size_t)(kt & 1) * STAGE;
+    const unsigned char* sb = sa + A_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < kGK; ks += 32) {
-      bf16x8 a[4], b[4];
+    for (int h = 0; h < 2; ++h) {
+      const int j = 4 * h + g;  // the lane's 16-byte chunk of the 128-byte row
+      bf16x8 b[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sA[cur][(wm + 16 * i + fr) * kGPitch + ks + fk]));
-        b[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sB[cur][(wn + 16 * i + fr) * kGPitch + ks + fk]));
+      for (int jn = 0; jn < NT; ++jn) {
+        const int r = wn0 + 16 * jn + fr;
+        b[jn] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + (r * 8 + (j ^ (r & 7))) * 16));
       }
+      // A fragments two at a time next to their MFMAs: beside the
+      // accumulators only the B fragments and two A fragments are live
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MT; i += 2) {
+        bf16x8 a[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          const int r = wm0 + 16 * (i + u) + fr;
+          a[u] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + (r * 8 + (j ^ (r & 7))) * 16));
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int jn = 0; jn < NT; ++jn)
+            acc[i + u][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[jn], acc[i + u][jn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (kt + 1 < nk) stash(cur ^ 1);
-    __syncthreads();
   }
 
-  // acc[i][j][e] holds C[m0 + wm + 16 i + 4 (lane >> 4) + e][n0 + wn + 16 j + (lane & 15)].
+  // acc[i][j][e] holds C[m0 + wm0 + 16 i + 4 g + e][n0 + wn0 + 16 j + fr].
+  // The output mode is uniform, so each mode gets its own store loop.
+  const int mb = m0 + wm0 + 4 * g;
+  if (p.mode == kOutResF32) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + wn + 16 * j + fr;
+    for (int jn = 0; jn < NT; ++jn) {
+      const int n = n0 + wn0 + 16 * jn + fr;
+      if (n >= p.N) continue;
+      const float bias = bf(p.bias, n);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = mb + 16 * i + e;
+          if (m >= p.M) continue;
+          const long long o = (long long)m * p.ldo + n;
+          p.out_f[o] = acc[i][jn][e] + bias + p.res[o];
+        }
+    }
+    return;
+  }
+  const bool relu = p.mode == kOutBf16Relu;
+#pragma unroll
+  for (int jn = 0; jn < NT; ++jn) {
+    const int n = n0 + wn0 + 16 * jn + fr;
     if (n >= p.N) continue;
     const float bias = bf(p.bias, n);
+    uint16_t* dst;
+    int ld;
+    if (n < p.tsplit) {
+      dst = p.out_bf + n;
+      ld = p.ldo;
+    } else if (p.vt == nullptr) {
+      dst = p.out2 + (n - p.tsplit);
+      ld = p.ld2;
+    } else {
+      // V^T per (crop, head): row c of head c / 64, keys along the row
+      const int c = n - p.tsplit;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = mb + 16 * i + e;
+          if (m >= p.M) continue;
+          const int b = m / p.t_rows, t = m - b * p.t_rows;
+          float v = acc[i][jn][e] + bias;
+          if (relu) v = fmaxf(v, 0.f);
+          p.vt[((long long)(b * p.nh + (c >> 6)) * kHd + (c & 63)) * p.vt_ld + t] = f32_to_bf16_bits(v);
+        }
+      continue;
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm + 16 * i + 4 * (lane >> 4) + e;
+        const int m = mb + 16 * i + e;
         if (m >= p.M) continue;
-        float v = acc[i][j][e] + bias;
-        if (p.mode == kOutResF32) {
-          const long long o = (long long)m * p.ldo + n;
-          p.out_f[o] = v + p.res[o];
-        } else {
-          if (p.mode == kOutBf16Relu) v = fmaxf(v, 0.f);
-          if (n < p.tsplit) {
-            p.out_bf[(long long)m * p.ldo + n] = f32_to_bf16_bits(v);
-          } else {
-            const int c = n - p.tsplit, b = m / p.t_rows, t = m % p.t_rows;
-            p.vt[((long long)(b * p.nh + (c >> 6)) * kHd + (c & 63)) * p.vt_ld + t] =
-                f32_to_bf16_bits(v);
-          }
-        }
+        float v = acc[i][jn][e] + bias;
+        if (relu) v = fmaxf(v, 0.f);
+        dst[(long long)m * ld] = f32_to_bf16_bits(v);
       }
-    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Attention of Tq queries over Tk <= 576 keys for one (crop, head), one
-// workgroup of 4 waves per (crop, head): K [Tk, 64] and V^T [64, Tk] of the
-// head are staged in LDS once (keys past Tk read as 0) and every wave reads
-// them there. A wave takes 16 queries at a time and computes the transposed scores S^T = K Q^T, so
+// Attention of the compact query rows of one crop (off[b] .. off[b+1]) over
+// Tk <= 576 keys, one workgroup of 4 waves per (crop, head). Keys: the
+// crop's own compact rows (self-attention; V row-major) or the crop's Tk
+// query-feature tokens (cross-attention; V given transposed per head).
+// K [Tk, 64] and V^T [64, Tk] of the head are staged in LDS once (keys past
+// Tk read as 0) and every wave reads them there. A wave takes 16 queries at
+// a time and computes the transposed scores S^T = K Q^T, so
 // lane (query n = lane & 15, group g = lane >> 4) holds keys 16 t + 4 g + e
 // (e = 0..3) of its query in tile t: 36 tiles cover 576 keys in registers.
 // Softmax (scale 1/sqrt(64)) reduces over e, t and the 4 lane groups. The
 // product O^T = V^T P^T then takes its P^T operand straight from those
 // registers: an MFMA sums over its 32 k-slots in any order as long as both
 // operands agree, so k-slots 8 g .. 8 g + 7 of a 32-key chunk c carry keys
-// 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3) on both sides. Keys with
-// key_ok == 0 get probability 0; a query without an allowed key gives 0.
+// 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3) on both sides. A crop
+// without compact rows has nothing to do.
 // ---------------------------------------------------------------------------
 struct AttnParams {
   const uint16_t* q;
   int ldq;
   const uint16_t* k;
   int ldk;
-  const uint16_t* vt;
+  const uint16_t* v;      // self-attention: V rows (row-major), or null
+  int ldv;
+  const uint16_t* vt;     // cross-attention: V^T per (crop, head), or null
   int vt_ld;
-  const uint8_t* key_ok;  // [B, Tk], or null: every key
+  const int* off;         // compact rows of crop b: off[b] .. off[b+1]
   uint16_t* out;
   int ldo;
-  int nh, Tq, Tk;
+  int nh, Tk;             // Tk: cross-attention keys per crop
 };
 
 constexpr int kAttnWaves = 4;
@@ -219,41 +311,59 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x % p.nh, b = blockIdx.x / p.nh;
   const int fr = lane & 15, g = lane >> 4, fk = g * 8;
-  const int nt = (p.Tk + 15) >> 4, kpad = rup32(p.Tk), vp = attn_vpitch(p.Tk);
+  const int qb = p.off[b], Tq = p.off[b + 1] - qb;
+  if (Tq <= 0) return;
+  const bool self = p.vt == nullptr;
+  const int Tk = self ? Tq : p.Tk;
+  const long long kb = self ? (long long)qb : (long long)b * p.Tk;  // first key row
+  const int nt = (Tk + 15) >> 4, kpad = rup32(Tk), vp = attn_vpitch(Tk);
   uint16_t* sK = lds_kv;
   uint16_t* sV = lds_kv + (size_t)nt * 16 * kKPitch;
 
   // Stage K (rows of 8 16-byte pieces) and V^T (64 rows of kpad keys).
-  for (int c = tid; c < p.Tk * 8; c += 64 * kAttnWaves) {
+  for (int c = tid; c < Tk * 8; c += 64 * kAttnWaves) {
     const int key = c >> 3, piece = (c & 7) * 8;
     *reinterpret_cast<u32x4*>(&sK[key * kKPitch + piece]) = *reinterpret_cast<const u32x4*>(
-        p.k + (long long)(b * p.Tk + key) * p.ldk + h * kHd + piece);
+        p.k + (kb + key) * p.ldk + h * kHd + piece);
   }
-  const uint16_t* vsrc = p.vt + (long long)(b * p.nh + h) * kHd * p.vt_ld;
-  for (int c = tid; c < kHd * (kpad / 8); c += 64 * kAttnWaves) {
-    const int d = c / (kpad / 8), k8 = (c % (kpad / 8)) * 8;
-    const uint16_t* src = vsrc + (long long)d * p.vt_ld + k8;
-    u32x4 v;
-    if (k8 + 8 <= p.Tk) {
-      v = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      uint32_t w[4];
+  if (self) {
+    // V rows -> V^T: 8 dims of one key per thread, scattered down 8 rows
+    for (int c = tid; c < kpad * 8; c += 64 * kAttnWaves) {
+      const int key = c >> 3, d0 = (c & 7) * 8;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (key < Tk) v = *reinterpret_cast<const u32x4*>(p.v + (kb + key) * p.ldv + h * kHd + d0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (k8 + 2 * e < p.Tk ? (uint32_t)src[2 * e] : 0u) |
-               ((k8 + 2 * e + 1 < p.Tk ? (uint32_t)src[2 * e + 1] : 0u) << 16);
-      v = u32x4{w[0], w[1], w[2], w[3]};
+      for (int e = 0; e < 4; ++e) {
+        sV[(d0 + 2 * e) * vp + key] = (uint16_t)(v[e] & 0xffffu);
+        sV[(d0 + 2 * e + 1) * vp + key] = (uint16_t)(v[e] >> 16);
+      }
     }
-    *reinterpret_cast<u32x4*>(&sV[d * vp + k8]) = v;
+  } else {
+    const uint16_t* vsrc = p.vt + (long long)(b * p.nh + h) * kHd * p.vt_ld;
+    for (int c = tid; c < kHd * (kpad / 8); c += 64 * kAttnWaves) {
+      const int d = c / (kpad / 8), k8 = (c % (kpad / 8)) * 8;
+      const uint16_t* src = vsrc + (long long)d * p.vt_ld + k8;
+      u32x4 v;
+      if (k8 + 8 <= Tk) {
+        v = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (k8 + 2 * e < Tk ? (uint32_t)src[2 * e] : 0u) |
+                 ((k8 + 2 * e + 1 < Tk ? (uint32_t)src[2 * e + 1] : 0u) << 16);
+        v = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      *reinterpret_cast<u32x4*>(&sV[d * vp + k8]) = v;
+    }
   }
   __syncthreads();
 
-  for (int q0 = wave * 16; q0 < p.Tq; q0 += 16 * kAttnWaves) {
+  for (int q0 = wave * 16; q0 < Tq; q0 += 16 * kAttnWaves) {
 
-  const uint16_t* qrow = p.q + (long long)(b * p.Tq + min(q0 + fr, p.Tq - 1)) * p.ldq + h * kHd + fk;
+  const uint16_t* qrow = p.q + (qb + min(q0 + fr, Tq - 1)) * (long long)p.ldq + h * kHd + fk;
   const bf16x8 qb0 = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow));
   const bf16x8 qb1 = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32));
-  const uint8_t* okrow = p.key_ok ? p.key_ok + (long long)b * p.Tk : nullptr;
 
   f32x4 s[NT];
   float mx = -INFINITY;
@@ -267,8 +377,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = t * 16 + 4 * g + e;
-        const bool ok = key < p.Tk && (!okrow || okrow[key]);
-        z[e] = ok ? z[e] : -INFINITY;
+        z[e] = key < Tk ? z[e] : -INFINITY;
         mx = fmaxf(mx, z[e]);
       }
       s[t] = z;
@@ -277,8 +386,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
 
-  // p = exp((s - max) / 8) = exp2((s - max) * log2(e) / 8); masked keys hold
-  // -inf and give 0, and so does every key of a query with no allowed key.
+  // p = exp((s - max) / 8) = exp2((s - max) * log2(e) / 8); keys past Tk
+  // hold -inf and give 0.
   constexpr float kScale = 0.125f * 1.4426950408889634f;
   const float base = mx == -INFINITY ? 0.f : mx;
   float sum = 0.f;
@@ -325,9 +434,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
   }
   // o[j][e] = O^T[dim 16 j + 4 g + e][query q0 + fr]
   const int qi = q0 + fr;
-  if (qi < p.Tq) {
+  if (qi < Tq) {
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    uint16_t* orow = p.out + (long long)(b * p.Tq + qi) * p.ldo + h * kHd + 4 * g;
+    uint16_t* orow = p.out + (qb + qi) * (long long)p.ldo + h * kHd + 4 * g;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w0 = f32_to_bf16_bits(o[j][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[j][1] * inv) << 16);
@@ -339,17 +448,20 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// LayerNorm of float32 rows (one wave per row, eps 1e-5, biased variance):
-// writes the float32 result (the residual stream) and its bfloat16 copy.
-// With R > 0 the bfloat16 rows go to the two-plane output instead: slot s
-// of crop b lands in row (s / R) * B + b, s % R of plane-major [2, B, R, C].
+// LayerNorm of the compact float32 rows m < *m_dev (one wave per row, eps
+// 1e-5, biased variance): writes the float32 result (the residual stream)
+// and its bfloat16 copy. With R > 0 the bfloat16 rows go to the two-plane
+// output instead: compact row m (crop cmap[m], slot smap[m]) lands in row
+// (slot / R) * B + b, slot % R of plane-major [2, B, R, C].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void kg_layernorm_kernel(const float* y, const uint16_t* w,
-                                                           const uint16_t* bvec, int M, int C,
-                                                           int B, int R, float* x, uint16_t* xb) {
+                                                           const uint16_t* bvec, const int* m_dev,
+                                                           int C, int B, int R, const int* cmap,
+                                                           const int* smap, float* x,
+                                                           uint16_t* xb) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
+  if (m >= *m_dev) return;
   const float* row = y + (long long)m * C;
   float s = 0.f;
   for (int c = lane; c < C; c += 64) s += row[c];
@@ -366,8 +478,8 @@ __global__ __launch_bounds__(256) void kg_layernorm_kernel(const float* y, const
   const float rs = 1.f / sqrtf(v / (float)C + 1e-5f);
   long long drow = m;
   if (R > 0) {
-    const int b = m / (2 * R), s = m % (2 * R);
-    drow = ((long long)(s >= R) * B + b) * R + (s >= R ? s - R : s);
+    const int b = cmap[m], sl = smap[m];
+    drow = ((long long)(sl >= R) * B + b) * R + (sl >= R ? sl - R : sl);
   }
   for (int c = lane; c < C; c += 64) {
     const float o = fmaf((row[c] - mu) * rs, bf(w, c), bf(bvec, c));
@@ -376,25 +488,72 @@ __global__ __launch_bounds__(256) void kg_layernorm_kernel(const float* y, const
   }
 }
 
-// The 2R input slots of every crop (prototype or mask token) and the
-// self-attention key mask (a slot is a key when its row has any prompt).
+// The compact slot list: crop b's n_b prompted rows (any mask set) give the
+// 2 n_b compact rows off[b] .. off[b+1] - 1, the visual slots (slot r) of
+// those rows in row order, then their text slots (slot R + r); cmap and
+// smap give each compact row's crop and slot, off[B] the row count. One
+// workgroup; crops in chunks of 1024 with a running carry.
+__global__ __launch_bounds__(1024) void kg_compact_kernel(const uint8_t* mv, const uint8_t* mt,
+                                                          int B, int R, int* off, int* cmap,
+                                                          int* smap) {
+  __shared__ int s_scan[1024];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 1024) {
+    const int b = b0 + tid;
+    auto prompted = [&](int r) {
+      const long long o = (long long)b * R + r;
+      return (mv && mv[o]) || (mt && mt[o]);
+    };
+    int n = 0;
+    if (b < B)
+      for (int r = 0; r < R; ++r) n += prompted(r) ? 1 : 0;
+    s_scan[tid] = n;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int add = tid >= d ? s_scan[tid - d] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    const int start = 2 * (carry + s_scan[tid] - n);
+    if (b < B) {
+      off[b] = start;
+      int j = 0;
+      for (int r = 0; r < R; ++r) {
+        if (!prompted(r)) continue;
+        cmap[start + j] = b;
+        smap[start + j] = r;
+        cmap[start + n + j] = b;
+        smap[start + n + j] = R + r;
+        ++j;
+      }
+    }
+    carry += s_scan[1023];
+    __syncthreads();  // s_scan is rewritten by the next chunk
+  }
+  if (tid == 0) off[B] = 2 * carry;
+}
+
+// The compact input rows: slot r < R of crop b holds its visual prototype
+// (slot R + r its text prototype), or the mask token where the row has no
+// prompt of that kind.
 __global__ void kg_assemble_kernel(const uint16_t* vis, const uint8_t* mv, const uint16_t* txt,
-                                   const uint8_t* mt, const uint16_t* tok, int B, int R, int C,
-                                   float* x, uint16_t* xb, uint8_t* key_ok) {
-  const long long n = (long long)B * 2 * R * C;
+                                   const uint8_t* mt, const uint16_t* tok, int R, int C,
+                                   const int* m_dev, const int* cmap, const int* smap, float* x,
+                                   uint16_t* xb) {
+  const long long n = (long long)(*m_dev) * C;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (long long)gridDim.x * blockDim.x) {
     const int c = (int)(i % C);
-    const long long bs = i / C;
-    const int s = (int)(bs % (2 * R)), b = (int)(bs / (2 * R));
-    const int r = s < R ? s : s - R;
+    const long long m = i / C;
+    const int b = cmap[m], sl = smap[m];
+    const int r = sl < R ? sl : sl - R;
     const long long row = (long long)b * R + r;
-    const bool v = mv && mv[row], t = mt && mt[row];
-    const bool have = s < R ? v : t;
-    const uint16_t h = have ? (s < R ? vis : txt)[row * C + c] : tok[c];
+    const bool have = sl < R ? (mv && mv[row]) : (mt && mt[row]);
+    const uint16_t h = have ? (sl < R ? vis : txt)[row * C + c] : tok[c];
     x[i] = bf16_bits_to_f32(h);
     xb[i] = h;
-    if (c == 0) key_ok[bs] = (v || t) ? 1 : 0;
   }
 }
 
@@ -420,14 +579,14 @@ __global__ __launch_bounds__(256) void kg_tokens_kernel(const uint16_t* src, int
 size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct KgWorkspace {
-  uint8_t* key_ok;
+  int *off, *cmap, *smap;
   float *x, *y;
   uint16_t *xb, *qk, *vt, *kc, *ao, *hh, *fq;
   size_t bytes;
 };
 
 KgWorkspace carve(uint8_t* base, int B, int C, int HW, int R, int F, bool tokens) {
-  const size_t M = (size_t)B * 2 * R, T = (size_t)rup32(2 * R > HW ? 2 * R : HW);
+  const size_t M = (size_t)B * 2 * R, T = (size_t)rup32(HW);
   KgWorkspace w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -435,7 +594,9 @@ KgWorkspace carve(uint8_t* base, int B, int C, int HW, int R, int F, bool tokens
     off += al256(bytes);
     return p;
   };
-  w.key_ok = take(M);
+  w.off = reinterpret_cast<int*>(take(((size_t)B + 1) * 4));
+  w.cmap = reinterpret_cast<int*>(take(M * 4));
+  w.smap = reinterpret_cast<int*>(take(M * 4));
   w.x = reinterpret_cast<float*>(take(M * C * 4));
   w.y = reinterpret_cast<float*>(take(M * C * 4));
   w.xb = reinterpret_cast<uint16_t*>(take(M * C * 2));
@@ -450,31 +611,39 @@ KgWorkspace carve(uint8_t* base, int B, int C, int HW, int R, int F, bool tokens
 }
 
 hipError_t gemm(const uint16_t* A, long long a_bstride, int a_rows, int lda, const uint16_t* W,
-                const uint16_t* bias, int M, int N, int K, int mode, uint16_t* out_bf,
-                float* out_f, const float* res, int ldo, int tsplit, uint16_t* vt, int t_rows,
-                int vt_ld, int nh, hipStream_t st) {
-  GemmParams p{A, a_bstride, a_rows, lda, W, bias, M, N, K, mode, out_bf, out_f, res, ldo,
-               tsplit, vt, t_rows, vt_ld, nh};
-  const int tiles = ((M + kGT - 1) / kGT) * ((N + kGT - 1) / kGT);
-  hipLaunchKernelGGL(kg_gemm_kernel, dim3(tiles), dim3(256), 0, st, p);
+                const uint16_t* bias, int M, const int* m_dev, int N, int K, int mode,
+                uint16_t* out_bf, float* out_f, const float* res, int ldo, int tsplit,
+                uint16_t* vt, int t_rows, int vt_ld, int nh, hipStream_t st,
+                uint16_t* out2 = nullptr, int ld2 = 0) {
+  GemmParams p{A, a_bstride, a_rows, lda, W, bias, M, N, K, m_dev, mode, out_bf, out_f, res, ldo,
+               tsplit, vt, t_rows, vt_ld, nh, out2, ld2};
+  // the wide tile where N fills it, else 128 columns
+  if (N % 256 == 0) {
+    const int tiles = ((M + kGM - 1) / kGM) * (N / 256);
+    hipLaunchKernelGGL(kg_gemm_kernel<256>, dim3(tiles), dim3(512), 2 * gemm_stage_bytes<256>(), st, p);
+  } else {
+    const int tiles = ((M + kGM - 1) / kGM) * ((N + 127) / 128);
+    hipLaunchKernelGGL(kg_gemm_kernel<128>, dim3(tiles), dim3(512), 2 * gemm_stage_bytes<128>(), st, p);
+  }
   return hipGetLastError();
 }
 
-hipError_t attn(const uint16_t* q, int ldq, const uint16_t* k, int ldk, const uint16_t* vt,
-                int vt_ld, const uint8_t* key_ok, uint16_t* out, int ldo, int B, int nh, int Tq,
-                int Tk, hipStream_t st) {
-  AttnParams p{q, ldq, k, ldk, vt, vt_ld, key_ok, out, ldo, nh, Tq, Tk};
-  if (Tk <= 160)
-    hipLaunchKernelGGL(kg_attn_kernel<10>, dim3(B * nh), dim3(64 * kAttnWaves), attn_lds_bytes(Tk), st, p);
+// tk_max: the most keys a crop can have (self-attention: 2R; cross: HW)
+hipError_t attn(const AttnParams& p, int B, int tk_max, hipStream_t st) {
+  if (tk_max <= 160)
+    hipLaunchKernelGGL(kg_attn_kernel<10>, dim3(B * p.nh), dim3(64 * kAttnWaves),
+                       attn_lds_bytes(tk_max), st, p);
   else
-    hipLaunchKernelGGL(kg_attn_kernel<kKeyTiles>, dim3(B * nh), dim3(64 * kAttnWaves), attn_lds_bytes(Tk), st, p);
+    hipLaunchKernelGGL(kg_attn_kernel<kKeyTiles>, dim3(B * p.nh), dim3(64 * kAttnWaves),
+                       attn_lds_bytes(tk_max), st, p);
   return hipGetLastError();
 }
 
-hipError_t layernorm(const float* y, const uint16_t* w, const uint16_t* b, int M, int C, int B,
-                     int R, float* x, uint16_t* xb, hipStream_t st) {
-  hipLaunchKernelGGL(kg_layernorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, y, w, b, M, C, B, R,
-                     x, xb);
+hipError_t layernorm(const float* y, const uint16_t* w, const uint16_t* b, int M,
+                     const int* m_dev, int C, int B, int R, const int* cmap, const int* smap,
+                     float* x, uint16_t* xb, hipStream_t st) {
+  hipLaunchKernelGGL(kg_layernorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, y, w, b, m_dev, C,
+                     B, R, cmap, smap, x, xb);
   return hipGetLastError();
 }
 
@@ -486,20 +655,24 @@ size_t kg_workspace_bytes(int B, int C, int H, int W, int R, int d_ff, bool toke
 
 hipError_t launch_kg(const KgArgs& a, hipStream_t st) {
   const int C = a.C, F = a.d_ff, R = a.R, HW = a.H * a.W, T = 2 * R, nh = C / kHd;
-  const int M = a.B * T;
+  const int M = a.B * T;  // rows the grids cover; the compact count off[B] bounds the work
   const KgWorkspace w = carve(static_cast<uint8_t*>(a.ws), a.B, C, HW, R, F, a.tokens);
+  const int* mc = w.off + a.B;
   const uint16_t* wts = static_cast<const uint16_t*>(a.weights);
   const uint16_t* tok = wts;
   const size_t blk = (size_t)8 * C * C + (size_t)2 * F * C + (size_t)15 * C + F;
-  const int vt_sa = rup32(T), vt_ca = rup32(HW);
+  const int vt_ca = rup32(HW);
 
   hipError_t e;
+  hipLaunchKernelGGL(kg_compact_kernel, dim3(1), dim3(1024), 0, st, a.mv, a.mt, a.B, R, w.off,
+                     w.cmap, w.smap);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   {
     const long long n = (long long)M * C;
     const int grid = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
     hipLaunchKernelGGL(kg_assemble_kernel, dim3(grid), dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.vis), a.mv, static_cast<const uint16_t*>(a.txt),
-                       a.mt, tok, a.B, R, C, w.x, w.xb, w.key_ok);
+                       a.mt, tok, R, C, mc, w.cmap, w.smap, w.x, w.xb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // The query features as a token matrix [B * HW, C] (read in place when
@@ -539,32 +712,42 @@ hipError_t launch_kg(const KgArgs& a, hipStream_t st) {
     const uint16_t* ln3_b = p;
     const bool last = l + 1 == a.n_blocks;
 
-    // self-attention
-    if ((e = gemm(w.xb, 0, M, C, sa_in_w, sa_in_b, M, 3 * C, C, kOutBf16, w.qk, nullptr, nullptr,
-                  2 * C, 2 * C, w.vt, T, vt_sa, nh, st)) != hipSuccess) return e;
-    if ((e = attn(w.qk, 2 * C, w.qk + C, 2 * C, w.vt, vt_sa, w.key_ok, w.ao, C, a.B, nh, T, T,
-                  st)) != hipSuccess) return e;
-    if ((e = gemm(w.ao, 0, M, C, sa_out_w, sa_out_b, M, C, C, kOutResF32, nullptr, w.y, w.x, C,
-                  C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
-    if ((e = layernorm(w.y, ln1_w, ln1_b, M, C, a.B, 0, w.x, w.xb, st)) != hipSuccess) return e;
+    // self-attention over the compact slots: [Q|K] rows, and V rows in the
+    // attention output buffer (each (crop, head) workgroup stages its V
+    // columns in LDS before it writes the same columns); keys = the crop's
+    // own slots
+    if ((e = gemm(w.xb, 0, M, C, sa_in_w, sa_in_b, M, mc, 3 * C, C, kOutBf16, w.qk, nullptr,
+                  nullptr, 2 * C, 2 * C, nullptr, 1, 1, nh, st, w.ao, C)) != hipSuccess) return e;
+    {
+      AttnParams ap{w.qk, 2 * C, w.qk + C, 2 * C, w.ao, C, nullptr, 0, w.off, w.ao, C, nh, 0};
+      if ((e = attn(ap, a.B, T, st)) != hipSuccess) return e;
+    }
+    if ((e = gemm(w.ao, 0, M, C, sa_out_w, sa_out_b, M, mc, C, C, kOutResF32, nullptr, w.y, w.x,
+                  C, C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+    if ((e = layernorm(w.y, ln1_w, ln1_b, M, mc, C, a.B, 0, w.cmap, w.smap, w.x, w.xb, st)) !=
+        hipSuccess) return e;
     // cross-attention to the query features
-    if ((e = gemm(w.xb, 0, M, C, ca_in_w, ca_in_b, M, C, C, kOutBf16, w.qk, nullptr, nullptr, C,
-                  C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
-    if ((e = gemm(fq, fq_bstride, HW, C, ca_in_w + (size_t)C * C, ca_in_b + C, a.B * HW, 2 * C,
-                  C, kOutBf16, w.kc, nullptr, nullptr, C, C, w.vt, HW, vt_ca, nh, st)) !=
+    if ((e = gemm(w.xb, 0, M, C, ca_in_w, ca_in_b, M, mc, C, C, kOutBf16, w.qk, nullptr, nullptr,
+                  C, C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+    if ((e = gemm(fq, fq_bstride, HW, C, ca_in_w + (size_t)C * C, ca_in_b + C, a.B * HW, nullptr,
+                  2 * C, C, kOutBf16, w.kc, nullptr, nullptr, C, C, w.vt, HW, vt_ca, nh, st)) !=
         hipSuccess) return e;
-    if ((e = attn(w.qk, C, w.kc, C, w.vt, vt_ca, nullptr, w.ao, C, a.B, nh, T, HW, st)) !=
+    {
+      AttnParams ap{w.qk, C, w.kc, C, nullptr, 0, w.vt, vt_ca, w.off, w.ao, C, nh, HW};
+      if ((e = attn(ap, a.B, HW, st)) != hipSuccess) return e;
+    }
+    if ((e = gemm(w.ao, 0, M, C, ca_out_w, ca_out_b, M, mc, C, C, kOutResF32, nullptr, w.y, w.x,
+                  C, C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+    if ((e = layernorm(w.y, ln2_w, ln2_b, M, mc, C, a.B, 0, w.cmap, w.smap, w.x, w.xb, st)) !=
         hipSuccess) return e;
-    if ((e = gemm(w.ao, 0, M, C, ca_out_w, ca_out_b, M, C, C, kOutResF32, nullptr, w.y, w.x, C,
-                  C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
-    if ((e = layernorm(w.y, ln2_w, ln2_b, M, C, a.B, 0, w.x, w.xb, st)) != hipSuccess) return e;
     // feed-forward
-    if ((e = gemm(w.xb, 0, M, C, ff1_w, ff1_b, M, F, C, kOutBf16Relu, w.hh, nullptr, nullptr, F,
-                  F, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
-    if ((e = gemm(w.hh, 0, M, F, ff2_w, ff2_b, M, C, F, kOutResF32, nullptr, w.y, w.x, C, C,
+    if ((e = gemm(w.xb, 0, M, C, ff1_w, ff1_b, M, mc, F, C, kOutBf16Relu, w.hh, nullptr, nullptr,
+                  F, F, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+    if ((e = gemm(w.hh, 0, M, F, ff2_w, ff2_b, M, mc, C, F, kOutResF32, nullptr, w.y, w.x, C, C,
                   nullptr, 1, 1, nh, st)) != hipSuccess) return e;
-    if ((e = layernorm(w.y, ln3_w, ln3_b, M, C, a.B, last ? R : 0, last ? nullptr : w.x,
-                       last ? static_cast<uint16_t*>(a.out) : w.xb, st)) != hipSuccess) return e;
+    if ((e = layernorm(w.y, ln3_w, ln3_b, M, mc, C, a.B, last ? R : 0, w.cmap, w.smap,
+                       last ? nullptr : w.x, last ? static_cast<uint16_t*>(a.out) : w.xb, st)) !=
+        hipSuccess) return e;
   }
   return hipSuccess;
 }

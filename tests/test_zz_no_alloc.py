@@ -53,9 +53,11 @@ def test_kg_noalloc_equals_workspace_call(gkd, tokens):
             q = torch.cat([torch.full((B, 5, C), 3.0, dtype=torch.bfloat16, device="cuda"), tok],
                           1).contiguous()
             kw = dict(token_hw=(H, W), token_skip=5)
-        ref = gkd.kg_transformer(q, w, kern_vis=vis, mask_vis=mv, kern_txt=txt, mask_txt=mt,
-                                 n_blocks=nb, d_ff=F, **kw)
-        out = torch.empty_like(ref).fill_(7.0)
+        # rows without a prompt are not written: both outputs start equal
+        ref = torch.full((2, B, R, C), 7.0, dtype=torch.bfloat16, device="cuda")
+        gkd.kg_transformer(q, w, kern_vis=vis, mask_vis=mv, kern_txt=txt, mask_txt=mt,
+                           n_blocks=nb, d_ff=F, out=ref, **kw)
+        out = torch.full_like(ref, 7.0)
         got = gkd.kg_transformer(q, w, kern_vis=vis, mask_vis=mv, kern_txt=txt, mask_txt=mt,
                                  n_blocks=nb, d_ff=F, out=out, workspace="static", **kw)
         torch.cuda.synchronize()
