@@ -22,10 +22,10 @@
 // bfloat16 throughout for matrix operands (weights, prototypes, features,
 // and every activation that feeds a product), float32 for accumulation, the
 // residual stream, softmax and LayerNorm. Per block:
-//   gemm   x -> [Q|K] rows and V^T per head        (SA in_proj)
+//   gemm   x -> [Q|K|V] rows                      (SA in_proj)
 //   attn   softmax(Q K^T / 8) V, scores in registers
 //   gemm   out_proj + bias + residual (float32)    -> LayerNorm
-//   gemm   x -> Q (CA), gemm F -> [K] rows and V^T (CA in_proj)
+//   gemm   x -> Q (CA), gemm F -> [K|V] rows       (CA in_proj)
 //   attn, gemm + residual -> LayerNorm
 //   gemm   W1 + bias, ReLU -> gemm W2 + bias + residual -> LayerNorm
 // The products run on v_mfma_f32_16x16x32_bf16.
@@ -51,10 +51,8 @@ __host__ __device__ __forceinline__ int rup32(int n) { return (n + 31) & ~31; }
 // C[m, n] = sum_k A[m, k] W[n, k] + bias[n], W a torch Linear weight [N, K].
 // Row m of A sits at A + (m / a_rows) * a_bstride + (m % a_rows) * lda, so a
 // token sequence with leading special tokens is read in place.
-// Epilogues: kOutBf16 (optionally ReLU); columns >= tsplit go to vt
-// transposed per head, vt[((b * nh + h) * 64 + d) * vt_ld + p] with
-// b = m / t_rows, p = m % t_rows, or (vt null) row-major to out2;
-// kOutResF32: float32 acc + bias + res.
+// Epilogues: kOutBf16 (optionally ReLU), columns >= tsplit row-major to
+// out2 instead; kOutResF32: float32 acc + bias + res.
 // ---------------------------------------------------------------------------
 enum { kOutBf16 = 0, kOutBf16Relu = 1, kOutResF32 = 2 };
 
@@ -72,9 +70,7 @@ struct GemmParams {
   const float* res;
   int ldo;
   int tsplit;
-  uint16_t* vt;
-  int t_rows, vt_ld, nh;
-  uint16_t* out2;  // with vt null: columns >= tsplit go here, row-major, ld2
+  uint16_t* out2;  // columns >= tsplit go here, row-major, ld2
   int ld2;
 };
 
@@ -110,17 +106,19 @@ __global__ __launch_bounds__(512) void kg_gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int total = gridDim.x;
-  int lin = blockIdx.x;
-  // Workgroups are dealt round-robin over the 8 XCDs; give each XCD a
-  // contiguous run of tiles so the N-tiles of one A row band share an L2.
-  if ((total & (kXcds - 1)) == 0) lin = (lin % kXcds) * (total / kXcds) + lin / kXcds;
+  // With a device-side row count the grid covers the most rows there can
+  // be and only the first `total` workgroups have tiles.
+  if (p.m_dev != nullptr) p.M = *p.m_dev;
+  const int total = ((p.M + kGM - 1) / kGM) * tiles_n;
+  const int bid = blockIdx.x;
+  if (bid >= total) return;
+  // Workgroups are dealt round-robin over the 8 XCDs (XCD bid % 8); give
+  // each XCD a contiguous run of the tiles, so the N-tiles of one A row
+  // band share an L2: XCD x takes tiles s_x .. s_x + c_x - 1 with
+  // c_x = total / 8 (+1 for the first total % 8).
+  const int xcd = bid % kXcds, q = total / kXcds, rem = total % kXcds;
+  const int lin = xcd * q + min(xcd, rem) + bid / kXcds;
   const int m0 = (lin / tiles_n) * kGM, n0 = (lin % tiles_n) * BN;
-  if (p.m_dev != nullptr) {
-    const int mr = *p.m_dev;  // compact rows: tiles past them have nothing to do
-    if (m0 >= mr) return;
-    p.M = mr;
-  }
 
   // per-lane element offsets of the chunks this lane loads (step 0)
   uint32_t aoff[NA], woff[NB];
@@ -189,114 +187,117 @@ __global__ __launch_bounds__(512) void kg_gemm_kernel(GemmParams p) {
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int jn = 0; jn < NT; ++jn)
-            acc[i + u][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[jn], acc[i + u][jn], 0, 0, 0);
+            acc[i + u][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[jn], a[u], acc[i + u][jn], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
-  // acc[i][j][e] holds C[m0 + wm0 + 16 i + 4 g + e][n0 + wn0 + 16 j + fr].
-  // The output mode is uniform, so each mode gets its own store loop.
-  const int mb = m0 + wm0 + 4 * g;
+  // The MFMAs compute the transposed tile (W rows as the first operand), so
+  // acc[i][j][e] holds C[m0 + wm0 + 16 i + fr][n0 + wn0 + 16 j + 4 g + e]:
+  // four consecutive columns of one row, stored as one 8- or 16-byte piece
+  // (N, tsplit and the leading dimensions are multiples of 64).
+  const int mrow = m0 + wm0 + fr;
+  const int nb = n0 + wn0 + 4 * g;
   if (p.mode == kOutResF32) {
 #pragma unroll
     for (int jn = 0; jn < NT; ++jn) {
-      const int n = n0 + wn0 + 16 * jn + fr;
+      const int n = nb + 16 * jn;
       if (n >= p.N) continue;
-      const float bias = bf(p.bias, n);
+      // the column group's residual loads first, then its stores
+      f32x4 r[MT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) {
+        const int m = mrow + 16 * i;
+        r[i] = m < p.M ? *reinterpret_cast<const f32x4*>(p.res + (long long)m * p.ldo + n)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const f32x4 bias = {bf(p.bias, n), bf(p.bias, n + 1), bf(p.bias, n + 2), bf(p.bias, n + 3)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = mb + 16 * i + e;
-          if (m >= p.M) continue;
-          const long long o = (long long)m * p.ldo + n;
-          p.out_f[o] = acc[i][jn][e] + bias + p.res[o];
-        }
+      for (int i = 0; i < MT; ++i) {
+        const int m = mrow + 16 * i;
+        if (m < p.M)
+          *reinterpret_cast<f32x4*>(p.out_f + (long long)m * p.ldo + n) = acc[i][jn] + bias + r[i];
+      }
     }
     return;
   }
   const bool relu = p.mode == kOutBf16Relu;
 #pragma unroll
   for (int jn = 0; jn < NT; ++jn) {
-    const int n = n0 + wn0 + 16 * jn + fr;
+    const int n = nb + 16 * jn;
     if (n >= p.N) continue;
-    const float bias = bf(p.bias, n);
+    const f32x4 bias = {bf(p.bias, n), bf(p.bias, n + 1), bf(p.bias, n + 2), bf(p.bias, n + 3)};
     uint16_t* dst;
     int ld;
     if (n < p.tsplit) {
       dst = p.out_bf + n;
       ld = p.ldo;
-    } else if (p.vt == nullptr) {
+    } else {
       dst = p.out2 + (n - p.tsplit);
       ld = p.ld2;
-    } else {
-      // V^T per (crop, head): row c of head c / 64, keys along the row
-      const int c = n - p.tsplit;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = mb + 16 * i + e;
-          if (m >= p.M) continue;
-          const int b = m / p.t_rows, t = m - b * p.t_rows;
-          float v = acc[i][jn][e] + bias;
-          if (relu) v = fmaxf(v, 0.f);
-          p.vt[((long long)(b * p.nh + (c >> 6)) * kHd + (c & 63)) * p.vt_ld + t] = f32_to_bf16_bits(v);
-        }
-      continue;
     }
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < MT; ++i) {
+      const int m = mrow + 16 * i;
+      if (m >= p.M) continue;
+      f32x4 v = acc[i][jn] + bias;
+      if (relu) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = mb + 16 * i + e;
-        if (m >= p.M) continue;
-        float v = acc[i][jn][e] + bias;
-        if (relu) v = fmaxf(v, 0.f);
-        dst[(long long)m * ld] = f32_to_bf16_bits(v);
+        for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
       }
+      const uint32_t w0 = f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+      const uint32_t w1 = f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+      *reinterpret_cast<u32x2*>(dst + (long long)m * ld) = u32x2{w0, w1};
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Attention of the compact query rows of one crop (off[b] .. off[b+1]) over
-// Tk <= 576 keys, one workgroup of 4 waves per (crop, head). Keys: the
-// crop's own compact rows (self-attention; V row-major) or the crop's Tk
-// query-feature tokens (cross-attention; V given transposed per head).
-// K [Tk, 64] and V^T [64, Tk] of the head are staged in LDS once (keys past
-// Tk read as 0) and every wave reads them there. A wave takes 16 queries at
-// a time and computes the transposed scores S^T = K Q^T, so
-// lane (query n = lane & 15, group g = lane >> 4) holds keys 16 t + 4 g + e
-// (e = 0..3) of its query in tile t: 36 tiles cover 576 keys in registers.
-// Softmax (scale 1/sqrt(64)) reduces over e, t and the 4 lane groups. The
-// product O^T = V^T P^T then takes its P^T operand straight from those
-// registers: an MFMA sums over its 32 k-slots in any order as long as both
-// operands agree, so k-slots 8 g .. 8 g + 7 of a 32-key chunk c carry keys
-// 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3) on both sides. A crop
-// without compact rows has nothing to do.
+// Tk <= 576 keys, one workgroup per (crop, head). Keys: the
+// crop's own compact rows (self-attention) or the crop's Tk query-feature
+// tokens (cross-attention); K and V are row-major in both cases. The
+// launches take it for self-attention; cross-attention streams its keys
+// (kg_xattn_kernel, below).
+// The head's K and V rows (128 bytes each, keys past Tk repeat the last
+// key, whose probability is 0) stream into LDS with global_load_lds, 16
+// bytes a lane and no register round trip; 16-byte chunk c of key row r
+// sits at chunk position c ^ (r & 7), so the 16 key rows one operand read
+// touches spread over the banks. A wave takes 16 queries at a time and
+// computes the transposed scores S^T = K Q^T, so lane (query n = lane & 15,
+// group g = lane >> 4) holds keys 16 t + 4 g + e (e = 0..3) of its query
+// in tile t: 36 tiles cover 576 keys in registers. Softmax (scale
+// 1/sqrt(64)) reduces over e, t and the 4 lane groups. The product
+// O^T = V^T P^T takes its P^T operand straight from those registers: an
+// MFMA sums over its 32 k-slots in any order as long as both operands
+// agree, so k-slots 8 g .. 8 g + 7 of a 32-key chunk c carry keys
+// 32 c + 4 g + (0..3) and 32 c + 16 + 4 g + (0..3) on both sides; the V^T
+// operand comes from row-major V through transposing LDS reads
+// (ds_read_b64_tr_b16: the 16 lanes of a group each point at 4 dims of one
+// of 4 key rows, and lane n receives the 4 keys of dim n). A crop without
+// compact rows has nothing to do.
 // ---------------------------------------------------------------------------
 struct AttnParams {
   const uint16_t* q;
   int ldq;
-  const uint16_t* k;
+  const uint16_t* k;      // K rows, head h at columns 64 h ..
   int ldk;
-  const uint16_t* v;      // self-attention: V rows (row-major), or null
+  const uint16_t* v;      // V rows, likewise
   int ldv;
-  const uint16_t* vt;     // cross-attention: V^T per (crop, head), or null
-  int vt_ld;
   const int* off;         // compact rows of crop b: off[b] .. off[b+1]
   uint16_t* out;
   int ldo;
-  int nh, Tk;             // Tk: cross-attention keys per crop
+  int nh, Tk;             // Tk: cross-attention keys per crop; 0: self-attention
 };
 
-constexpr int kAttnWaves = 4;
-constexpr int kKPitch = kHd + 8;  // bf16 per LDS row of K (16-B rows, skewed banks)
+// Waves per workgroup: 8 where the key tiles leave room for two waves a
+// SIMD (NT = 10), 4 for 576 keys, whose scores need most of a SIMD's registers.
+template <int NT>
+constexpr int attn_waves() { return NT <= 10 ? 8 : 4; }
 
-__host__ __device__ inline int attn_vpitch(int Tk) { return rup32(Tk) + 8; }
-__host__ __device__ inline size_t attn_lds_bytes(int Tk) {
-  return (size_t)((Tk + 15) & ~15) * kKPitch * 2 + (size_t)kHd * attn_vpitch(Tk) * 2;
+__host__ __device__ inline size_t attn_lds_bytes(int tk_max) {
+  return (size_t)rup32(tk_max) * kHd * 2 * 2;  // K and V rows
 }
 
 // bfloat16 bits of a float, round to nearest even (v_cvt_pk_bf16_f32).
@@ -304,60 +305,41 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 // NT: key tiles held in registers (10 covers 160 keys, 36 covers 576).
 template <int NT>
-__global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds_kv[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(64 * attn_waves<NT>()) void kg_attn_kernel(AttnParams p) {
+  constexpr int kAttnWaves = attn_waves<NT>();
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_kv[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x % p.nh, b = blockIdx.x / p.nh;
   const int fr = lane & 15, g = lane >> 4, fk = g * 8;
   const int qb = p.off[b], Tq = p.off[b + 1] - qb;
   if (Tq <= 0) return;
-  const bool self = p.vt == nullptr;
+  const bool self = p.Tk == 0;
   const int Tk = self ? Tq : p.Tk;
   const long long kb = self ? (long long)qb : (long long)b * p.Tk;  // first key row
-  const int nt = (Tk + 15) >> 4, kpad = rup32(Tk), vp = attn_vpitch(Tk);
-  uint16_t* sK = lds_kv;
-  uint16_t* sV = lds_kv + (size_t)nt * 16 * kKPitch;
+  const int nt = (Tk + 15) >> 4, kpad = rup32(Tk);
+  unsigned char* sK = lds_kv;
+  unsigned char* sV = lds_kv + (size_t)kpad * 128;
 
-  // Stage K (rows of 8 16-byte pieces) and V^T (64 rows of kpad keys).
-  for (int c = tid; c < Tk * 8; c += 64 * kAttnWaves) {
-    const int key = c >> 3, piece = (c & 7) * 8;
-    *reinterpret_cast<u32x4*>(&sK[key * kKPitch + piece]) = *reinterpret_cast<const u32x4*>(
-        p.k + (kb + key) * p.ldk + h * kHd + piece);
+  // Stage K, then V: 1-KiB blocks of 8 key rows, one block per wave and
+  // instruction.
+  const int nblk = kpad / 8;
+  for (int blk = wave; blk < 2 * nblk; blk += kAttnWaves) {
+    const bool isv = blk >= nblk;
+    const int bl = isv ? blk - nblk : blk;
+    const int q = bl * 64 + lane, r = q >> 3, c = (q & 7) ^ (r & 7);
+    const long long key = kb + min(r, Tk - 1);
+    const uint16_t* src = (isv ? p.v + key * p.ldv : p.k + key * p.ldk) + h * kHd + 8 * c;
+    __builtin_amdgcn_global_load_lds((kg_glb_void*)src, (kg_lds_void*)((isv ? sV : sK) + bl * 1024),
+                                     16, 0, 0);
   }
-  if (self) {
-    // V rows -> V^T: 8 dims of one key per thread, scattered down 8 rows
-    for (int c = tid; c < kpad * 8; c += 64 * kAttnWaves) {
-      const int key = c >> 3, d0 = (c & 7) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (key < Tk) v = *reinterpret_cast<const u32x4*>(p.v + (kb + key) * p.ldv + h * kHd + d0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sV[(d0 + 2 * e) * vp + key] = (uint16_t)(v[e] & 0xffffu);
-        sV[(d0 + 2 * e + 1) * vp + key] = (uint16_t)(v[e] >> 16);
-      }
-    }
-  } else {
-    const uint16_t* vsrc = p.vt + (long long)(b * p.nh + h) * kHd * p.vt_ld;
-    for (int c = tid; c < kHd * (kpad / 8); c += 64 * kAttnWaves) {
-      const int d = c / (kpad / 8), k8 = (c % (kpad / 8)) * 8;
-      const uint16_t* src = vsrc + (long long)d * p.vt_ld + k8;
-      u32x4 v;
-      if (k8 + 8 <= Tk) {
-        v = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = (k8 + 2 * e < Tk ? (uint32_t)src[2 * e] : 0u) |
-                 ((k8 + 2 * e + 1 < Tk ? (uint32_t)src[2 * e + 1] : 0u) << 16);
-        v = u32x4{w[0], w[1], w[2], w[3]};
-      }
-      *reinterpret_cast<u32x4*>(&sV[d * vp + k8]) = v;
-    }
-  }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);  // vmcnt(0): this wave's blocks landed
+  __syncthreads();                              // and everyone's
 
   for (int q0 = wave * 16; q0 < Tq; q0 += 16 * kAttnWaves) {
 
@@ -369,15 +351,19 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    if ((t & 3) == 0) __builtin_amdgcn_sched_barrier(0);  // K reads a few tiles ahead, not all
     if (t < nt) {
-      const uint16_t* krow = sK + (t * 16 + fr) * kKPitch + fk;  // rows past Tk: masked below
+      const int key = t * 16 + fr;  // rows past Tk: masked below
+      const unsigned char* krow = sK + key * 128;
+      const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + ((g ^ (key & 7)) << 4)));
+      const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + (((g + 4) ^ (key & 7)) << 4)));
       f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(krow)), qb0, z, 0, 0, 0);
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32)), qb1, z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb0, z, 0, 0, 0);
+      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb1, z, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int key = t * 16 + 4 * g + e;
-        z[e] = key < Tk ? z[e] : -INFINITY;
+        const int kk = t * 16 + 4 * g + e;
+        z[e] = kk < Tk ? z[e] : -INFINITY;
         mx = fmaxf(mx, z[e]);
       }
       s[t] = z;
@@ -416,18 +402,26 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
   f32x4 o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* vbase = sV + 4 * g;
+  // lane (fr, g) points at key row 4 g + fr / 4 of the chunk, dims
+  // 16 j + 4 (fr % 4) .. + 3; the keys 16 further share the row swizzle
+  const int vkey = 4 * g + (fr >> 2);
 #pragma unroll
   for (int c = 0; c < (NT + 1) / 2; ++c) {
+    // keep the V reads of each chunk beside its MFMAs (hoisted, they would
+    // sit in registers next to all of P)
+    __builtin_amdgcn_sched_barrier(0);
     if (2 * c < nt) {
       const bf16x8 pb = as_bf16x8(u32x4{pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]});
-      const int k0 = 32 * c;
+      const int key = 32 * c + vkey;
+      const unsigned char* vrow = sV + key * 128 + (fr & 1) * 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint16_t* vrow = vbase + (16 * j + fr) * vp + k0;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
-        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        const int chunk = 2 * j + ((fr & 3) >> 1);
+        const unsigned char* a = vrow + ((chunk ^ (key & 7)) << 4);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 16 * 128));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 va = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
         o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[j], 0, 0, 0);
       }
     }
@@ -445,6 +439,159 @@ __global__ __launch_bounds__(64 * kAttnWaves) void kg_attn_kernel(AttnParams p) 
     }
   }
   }  // query groups
+}
+
+// ---------------------------------------------------------------------------
+// Cross-attention with the keys streamed: the same product as above for
+// Tk = HW keys (the crop's query-feature tokens), one workgroup of 8 waves
+// per (crop, head), but K and V pass through a three-stage LDS ring in
+// chunks of 64 keys (16 KiB a stage, global_load_lds, same swizzle), so a
+// workgroup needs 48 KiB and several share a CU, one's loads overlapping
+// another's products. Softmax runs online (Milakov and Gimelshein, "Online
+// normalizer calculation for softmax"): per chunk the running maximum m of
+// a query moves to max(m, chunk max), the sum l and the output O are scaled
+// by exp((m_old - m_new) / 8) and the chunk's probabilities
+// exp((s - m_new) / 8), rounded to bfloat16, are added to l and, through
+// the MFMA, to O. Wave w owns query tile w of each pass of 128 queries
+// (one tile a wave keeps two workgroups on a CU).
+// ---------------------------------------------------------------------------
+constexpr int kXaWaves = 8, kXaChunk = 64, kXaStages = 3;
+constexpr int kXaStage = 2 * kXaChunk * 128;  // K rows, then V rows
+constexpr int kXaQt = 1;                     // query tiles a wave holds
+
+__global__ __launch_bounds__(64 * kXaWaves) void kg_xattn_kernel(AttnParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_ring[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x % p.nh, b = blockIdx.x / p.nh;
+  const int fr = lane & 15, g = lane >> 4, fk = g * 8;
+  const int qb = p.off[b], Tq = p.off[b + 1] - qb;
+  if (Tq <= 0) return;
+  const int Tk = p.Tk;
+  const long long kb = (long long)b * Tk;
+  const int nch = (Tk + kXaChunk - 1) / kXaChunk;
+  const int nqt = (Tq + 15) >> 4;
+  constexpr float kScale = 0.125f * 1.4426950408889634f;
+
+  // wave w loads K rows 8 w .. 8 w + 7 and V rows 8 w .. 8 w + 7 of a chunk
+  const int dr = 8 * wave + (lane >> 3), dc = (lane & 7) ^ (dr & 7);
+  auto issue = [&](int ch) {
+    unsigned char* st = lds_ring + (ch % kXaStages) * kXaStage;
+    const long long key = kb + min(ch * kXaChunk + dr, Tk - 1);
+    __builtin_amdgcn_global_load_lds((kg_glb_void*)(p.k + key * p.ldk + h * kHd + 8 * dc),
+                                     (kg_lds_void*)(st + wave * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((kg_glb_void*)(p.v + key * p.ldv + h * kHd + 8 * dc),
+                                     (kg_lds_void*)(st + kXaChunk * 128 + wave * 1024), 16, 0, 0);
+  };
+
+  for (int qt0 = 0; qt0 < nqt; qt0 += kXaWaves * kXaQt) {
+    __syncthreads();  // the previous pass is done with the ring
+    bf16x8 qf[kXaQt][2];
+    f32x4 o[kXaQt][4];
+    float m[kXaQt], l[kXaQt];
+#pragma unroll
+    for (int u = 0; u < kXaQt; ++u) {
+      const int q0 = (qt0 + wave + kXaWaves * u) * 16;
+      const uint16_t* qrow = p.q + (qb + min(q0 + fr, Tq - 1)) * (long long)p.ldq + h * kHd + fk;
+      qf[u][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow));
+      qf[u][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[u] = -INFINITY;
+      l[u] = 0.f;
+    }
+    issue(0);
+    if (nch > 1) issue(1);
+    for (int ch = 0; ch < nch; ++ch) {
+      // this chunk's two loads landed (the next chunk's two may still fly)
+      if (ch + 1 < nch)
+        __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00 | 2);  // vmcnt(2)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);      // vmcnt(0)
+      __syncthreads();  // everyone's landed; stage (ch + 2) % 3 is free
+      if (ch + 2 < nch) issue(ch + 2);
+      const unsigned char* sK = lds_ring + (ch % kXaStages) * kXaStage;
+      const unsigned char* sV = sK + kXaChunk * 128;
+#pragma unroll
+      for (int u = 0; u < kXaQt; ++u) {
+        if (qt0 + wave + kXaWaves * u >= nqt) continue;  // wave-uniform
+        f32x4 sc[4];
+        float cm = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kr = t * 16 + fr;
+          const unsigned char* krow = sK + kr * 128;
+          const bf16x8 k0 = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + ((g ^ (kr & 7)) << 4)));
+          const bf16x8 k1 = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + (((g + 4) ^ (kr & 7)) << 4)));
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[u][0], z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[u][1], z, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            z[e] = ch * kXaChunk + t * 16 + 4 * g + e < Tk ? z[e] : -INFINITY;
+            cm = fmaxf(cm, z[e]);
+          }
+          sc[t] = z;
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        const float mn = fmaxf(m[u], cm);  // finite: every chunk has a key
+        const float alpha = __builtin_amdgcn_exp2f((m[u] - mn) * kScale);  // 0 on the first chunk
+        m[u] = mn;
+        uint32_t pk[4][2];
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          uint32_t hb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hb[e] = bf16_rne(__builtin_amdgcn_exp2f((sc[t][e] - mn) * kScale));
+            ps += bf16_bits_to_f32(hb[e]);
+          }
+          pk[t][0] = hb[0] | (hb[1] << 16);
+          pk[t][1] = hb[2] | (hb[3] << 16);
+        }
+        l[u] = l[u] * alpha + ps;  // this lane's share; the groups are summed at the end
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[u][j] *= alpha;
+        const int vkey = 4 * g + (fr >> 2);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pb = as_bf16x8(u32x4{pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]});
+          const int kr = 32 * c + vkey;
+          const unsigned char* vrow = sV + kr * 128 + (fr & 1) * 8;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int chunk = 2 * j + ((fr & 3) >> 1);
+            const unsigned char* a = vrow + ((chunk ^ (kr & 7)) << 4);
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 16 * 128));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            o[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]}),
+                                                            pb, o[u][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // o[u][j][e] = O^T[dim 16 j + 4 g + e][query]: normalise and store
+#pragma unroll
+    for (int u = 0; u < kXaQt; ++u) {
+      float sum = l[u];
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const int qi = (qt0 + wave + kXaWaves * u) * 16 + fr;
+      if (qi < Tq) {
+        const float inv = sum > 0.f ? 1.f / sum : 0.f;
+        uint16_t* orow = p.out + (qb + qi) * (long long)p.ldo + h * kHd + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = f32_to_bf16_bits(o[u][j][0] * inv) | ((uint32_t)f32_to_bf16_bits(o[u][j][1] * inv) << 16);
+          const uint32_t w1 = f32_to_bf16_bits(o[u][j][2] * inv) | ((uint32_t)f32_to_bf16_bits(o[u][j][3] * inv) << 16);
+          *reinterpret_cast<u32x2*>(orow + 16 * j) = u32x2{w0, w1};
+        }
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -581,12 +728,12 @@ size_t al256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct KgWorkspace {
   int *off, *cmap, *smap;
   float *x, *y;
-  uint16_t *xb, *qk, *vt, *kc, *ao, *hh, *fq;
+  uint16_t *xb, *qk, *kv, *ao, *hh, *fq;
   size_t bytes;
 };
 
 KgWorkspace carve(uint8_t* base, int B, int C, int HW, int R, int F, bool tokens) {
-  const size_t M = (size_t)B * 2 * R, T = (size_t)rup32(HW);
+  const size_t M = (size_t)B * 2 * R;
   KgWorkspace w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -601,8 +748,7 @@ KgWorkspace carve(uint8_t* base, int B, int C, int HW, int R, int F, bool tokens
   w.y = reinterpret_cast<float*>(take(M * C * 4));
   w.xb = reinterpret_cast<uint16_t*>(take(M * C * 2));
   w.qk = reinterpret_cast<uint16_t*>(take(M * 2 * C * 2));
-  w.vt = reinterpret_cast<uint16_t*>(take((size_t)B * C * T * 2));
-  w.kc = reinterpret_cast<uint16_t*>(take((size_t)B * HW * C * 2));
+  w.kv = reinterpret_cast<uint16_t*>(take((size_t)B * HW * 2 * C * 2));
   w.ao = reinterpret_cast<uint16_t*>(take(M * C * 2));
   w.hh = reinterpret_cast<uint16_t*>(take(M * F * 2));
   w.fq = tokens ? nullptr : reinterpret_cast<uint16_t*>(take((size_t)B * HW * C * 2));
@@ -613,10 +759,9 @@ KgWorkspace carve(uint8_t* base, int B, int C, int HW, int R, int F, bool tokens
 hipError_t gemm(const uint16_t* A, long long a_bstride, int a_rows, int lda, const uint16_t* W,
                 const uint16_t* bias, int M, const int* m_dev, int N, int K, int mode,
                 uint16_t* out_bf, float* out_f, const float* res, int ldo, int tsplit,
-                uint16_t* vt, int t_rows, int vt_ld, int nh, hipStream_t st,
-                uint16_t* out2 = nullptr, int ld2 = 0) {
+                hipStream_t st, uint16_t* out2 = nullptr, int ld2 = 0) {
   GemmParams p{A, a_bstride, a_rows, lda, W, bias, M, N, K, m_dev, mode, out_bf, out_f, res, ldo,
-               tsplit, vt, t_rows, vt_ld, nh, out2, ld2};
+               tsplit, out2, ld2};
   // the wide tile where N fills it, else 128 columns
   if (N % 256 == 0) {
     const int tiles = ((M + kGM - 1) / kGM) * (N / 256);
@@ -630,11 +775,14 @@ hipError_t gemm(const uint16_t* A, long long a_bstride, int a_rows, int lda, con
 
 // tk_max: the most keys a crop can have (self-attention: 2R; cross: HW)
 hipError_t attn(const AttnParams& p, int B, int tk_max, hipStream_t st) {
-  if (tk_max <= 160)
-    hipLaunchKernelGGL(kg_attn_kernel<10>, dim3(B * p.nh), dim3(64 * kAttnWaves),
+  if (p.Tk > 0)
+    hipLaunchKernelGGL(kg_xattn_kernel, dim3(B * p.nh), dim3(64 * kXaWaves),
+                       kXaStages * kXaStage, st, p);
+  else if (tk_max <= 160)
+    hipLaunchKernelGGL(kg_attn_kernel<10>, dim3(B * p.nh), dim3(64 * attn_waves<10>()),
                        attn_lds_bytes(tk_max), st, p);
   else
-    hipLaunchKernelGGL(kg_attn_kernel<kKeyTiles>, dim3(B * p.nh), dim3(64 * kAttnWaves),
+    hipLaunchKernelGGL(kg_attn_kernel<kKeyTiles>, dim3(B * p.nh), dim3(64 * attn_waves<kKeyTiles>()),
                        attn_lds_bytes(tk_max), st, p);
   return hipGetLastError();
 }
@@ -661,7 +809,6 @@ hipError_t launch_kg(const KgArgs& a, hipStream_t st) {
   const uint16_t* wts = static_cast<const uint16_t*>(a.weights);
   const uint16_t* tok = wts;
   const size_t blk = (size_t)8 * C * C + (size_t)2 * F * C + (size_t)15 * C + F;
-  const int vt_ca = rup32(HW);
 
   hipError_t e;
   hipLaunchKernelGGL(kg_compact_kernel, dim3(1), dim3(1024), 0, st, a.mv, a.mt, a.B, R, w.off,
@@ -717,34 +864,34 @@ hipError_t launch_kg(const KgArgs& a, hipStream_t st) {
     // columns in LDS before it writes the same columns); keys = the crop's
     // own slots
     if ((e = gemm(w.xb, 0, M, C, sa_in_w, sa_in_b, M, mc, 3 * C, C, kOutBf16, w.qk, nullptr,
-                  nullptr, 2 * C, 2 * C, nullptr, 1, 1, nh, st, w.ao, C)) != hipSuccess) return e;
+                  nullptr, 2 * C, 2 * C, st, w.ao, C)) != hipSuccess) return e;
     {
-      AttnParams ap{w.qk, 2 * C, w.qk + C, 2 * C, w.ao, C, nullptr, 0, w.off, w.ao, C, nh, 0};
+      AttnParams ap{w.qk, 2 * C, w.qk + C, 2 * C, w.ao, C, w.off, w.ao, C, nh, 0};
       if ((e = attn(ap, a.B, T, st)) != hipSuccess) return e;
     }
     if ((e = gemm(w.ao, 0, M, C, sa_out_w, sa_out_b, M, mc, C, C, kOutResF32, nullptr, w.y, w.x,
-                  C, C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+                  C, C, st)) != hipSuccess) return e;
     if ((e = layernorm(w.y, ln1_w, ln1_b, M, mc, C, a.B, 0, w.cmap, w.smap, w.x, w.xb, st)) !=
         hipSuccess) return e;
-    // cross-attention to the query features
+    // cross-attention to the query features: [K|V] rows of every token
     if ((e = gemm(w.xb, 0, M, C, ca_in_w, ca_in_b, M, mc, C, C, kOutBf16, w.qk, nullptr, nullptr,
-                  C, C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+                  C, C, st)) != hipSuccess) return e;
     if ((e = gemm(fq, fq_bstride, HW, C, ca_in_w + (size_t)C * C, ca_in_b + C, a.B * HW, nullptr,
-                  2 * C, C, kOutBf16, w.kc, nullptr, nullptr, C, C, w.vt, HW, vt_ca, nh, st)) !=
-        hipSuccess) return e;
+                  2 * C, C, kOutBf16, w.kv, nullptr, nullptr, 2 * C, 2 * C, st)) != hipSuccess)
+      return e;
     {
-      AttnParams ap{w.qk, C, w.kc, C, nullptr, 0, w.vt, vt_ca, w.off, w.ao, C, nh, HW};
+      AttnParams ap{w.qk, C, w.kv, 2 * C, w.kv + C, 2 * C, w.off, w.ao, C, nh, HW};
       if ((e = attn(ap, a.B, HW, st)) != hipSuccess) return e;
     }
     if ((e = gemm(w.ao, 0, M, C, ca_out_w, ca_out_b, M, mc, C, C, kOutResF32, nullptr, w.y, w.x,
-                  C, C, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+                  C, C, st)) != hipSuccess) return e;
     if ((e = layernorm(w.y, ln2_w, ln2_b, M, mc, C, a.B, 0, w.cmap, w.smap, w.x, w.xb, st)) !=
         hipSuccess) return e;
     // feed-forward
     if ((e = gemm(w.xb, 0, M, C, ff1_w, ff1_b, M, mc, F, C, kOutBf16Relu, w.hh, nullptr, nullptr,
-                  F, F, nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+                  F, F, st)) != hipSuccess) return e;
     if ((e = gemm(w.hh, 0, M, F, ff2_w, ff2_b, M, mc, C, F, kOutResF32, nullptr, w.y, w.x, C, C,
-                  nullptr, 1, 1, nh, st)) != hipSuccess) return e;
+                  st)) != hipSuccess) return e;
     if ((e = layernorm(w.y, ln3_w, ln3_b, M, mc, C, a.B, last ? R : 0, w.cmap, w.smap,
                        last ? nullptr : w.x, last ? static_cast<uint16_t*>(a.out) : w.xb, st)) !=
         hipSuccess) return e;
