@@ -77,31 +77,46 @@ struct GemmParams {
 typedef __attribute__((address_space(3))) void kg_lds_void;
 typedef __attribute__((address_space(1))) void kg_glb_void;
 
-// Workgroup tile 256 x BN, K step 64, 8 waves: BN = 256 as 2 x 4 wave tiles
-// of 128 x 64, BN = 128 as 4 x 2 wave tiles of 64 x 64 (MT x 4 MFMA tiles
-// of 16 x 16 per wave). Both operand tiles stream straight into LDS
-// (global_load_lds, 16 bytes a lane): row r of a tile is 128 bytes, eight
-// 16-byte chunks, and chunk c of row r is stored at chunk position
-// c ^ (r & 7), so the 16 rows an MFMA operand read touches fall in
-// different banks. Two stages: the loads of K step k + 1 are issued right
-// after the barrier of step k and land while step k computes.
-constexpr int kGM = 256, kGK = 64;
+// Workgroup tile 256 x BN, K step BK (32 or 64), 8 waves: BN = 256 as
+// 2 x 4 wave tiles of 128 x 64, BN = 128 as 4 x 2 wave tiles of 64 x 64
+// (MT x 4 MFMA tiles of 16 x 16 per wave). Both operand tiles stream
+// straight into LDS (global_load_lds, 16 bytes a lane) through a ring of NS
+// stages, the loads of K step k + NS - 1 issued right after the barrier of
+// step k. Row r of a tile is BK / 8 16-byte chunks; chunk c sits at chunk
+// position c ^ sw(r), sw(r) = r & 7 for 8 chunks a row and (r >> 2) & 3 for
+// 4, so the 16 rows an MFMA operand read touches fall in different banks.
+constexpr int kGM = 256;
+constexpr int kGemmBK = 64, kGemmNS = 2;
 
-template <int BN>
-__host__ __device__ constexpr size_t gemm_stage_bytes() {
-  return (size_t)(kGM + BN) * kGK * 2;
+template <int BN, int BK, int NS>
+__host__ __device__ constexpr size_t gemm_lds_bytes() {
+  return (size_t)NS * (kGM + BN) * BK * 2;
 }
 
-template <int BN>
+template <int CPR>
+__device__ __forceinline__ int gemm_sw(int r) {
+  return CPR == 8 ? (r & 7) : ((r >> 2) & 3);
+}
+
+// s_waitcnt vmcnt(N) (N < 64), the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int BN, int BK, int NS>
 __global__ __launch_bounds__(512) void kg_gemm_kernel(GemmParams p) {
   constexpr int WM = BN == 256 ? 128 : 64;  // wave tile rows
   constexpr int MT = WM / 16;
   constexpr int NT = 4;                     // wave tile columns: 64
   constexpr int WN = BN / 64;               // waves across N
-  constexpr int A_BYTES = kGM * kGK * 2;
-  constexpr int STAGE = (kGM + BN) * kGK * 2;
-  constexpr int NA = kGM * 8 / 64 / 8;      // A loads per wave and step (16-B chunks / 64 lanes / 8 waves)
-  constexpr int NB = BN * 8 / 64 / 8;
+  constexpr int CPR = BK / 8;               // 16-byte chunks a row
+  constexpr int A_BYTES = kGM * BK * 2;
+  constexpr int STAGE = (kGM + BN) * BK * 2;
+  constexpr int NA = kGM * CPR / 512;       // A loads per wave and step (64 lanes x 8 waves)
+  constexpr int NB = BN * CPR / 512;
+  constexpr int PS = NA + NB;               // loads per wave and stage
+  static_assert(NS >= 2 && NS <= 4 && PS * (NS - 2) < 16, "ring shape");
   extern __shared__ __attribute__((aligned(16))) unsigned char glds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,14 +139,14 @@ __global__ __launch_bounds__(512) void kg_gemm_kernel(GemmParams p) {
   uint32_t aoff[NA], woff[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int q = (wave + 8 * i) * 64 + lane, r = q >> 3, cs = (q & 7) ^ (r & 7);
+    const int q = (wave + 8 * i) * 64 + lane, r = q / CPR, cs = (q % CPR) ^ gemm_sw<CPR>(r);
     const int m = min(m0 + r, p.M - 1);
     aoff[i] = (uint32_t)((long long)(m / p.a_rows) * p.a_bstride + (long long)(m % p.a_rows) * p.lda +
                          8 * cs);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int q = (wave + 8 * i) * 64 + lane, r = q >> 3, cs = (q & 7) ^ (r & 7);
+    const int q = (wave + 8 * i) * 64 + lane, r = q / CPR, cs = (q % CPR) ^ gemm_sw<CPR>(r);
     const int n = min(n0 + r, p.N - 1);
     woff[i] = (uint32_t)((long long)n * p.K + 8 * cs);
   }
@@ -156,40 +171,57 @@ __global__ __launch_bounds__(512) void kg_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / kGK;
-  issue(0, 0);
+  const int nk = p.K / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s, s * BK);
+  int slot = 0;  // kt % NS
   for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);  // vmcnt(0): this step's loads landed
-    __syncthreads();                              // everyone's; the other stage is free
-    if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kGK);
-    const unsigned char* sa = glds + (size_t)(kt & 1) * STAGE;
+    // this step's loads landed; later steps' (up to NS - 2 of them) may fly
+    const int later = min(NS - 2, nk - 1 - kt);
+    if (NS > 3 && later >= 2) wait_vmcnt<2 * PS>();
+    else if (NS > 2 && later >= 1) wait_vmcnt<PS>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // everyone's; the slot step kt - 1 used is free
+    if (kt + NS - 1 < nk) issue(slot == 0 ? NS - 1 : slot - 1, (kt + NS - 1) * BK);
+    const unsigned char* sa = glds + (size_t)slot * STAGE;
     const unsigned char* sb = sa + A_BYTES;
+    slot = slot + 1 == NS ? 0 : slot + 1;
+    // Operand fragments run one group ahead of the MFMAs that use them: a
+    // group is two A fragments (rows 16 i .. 16 i + 31 of the wave tile)
+    // times the four B fragments of one 32-wide K half, and the loads for
+    // group n + 1 are issued before the MFMAs of group n, so their LDS
+    // latency hides behind those MFMAs.
+    constexpr int GPH = MT / 2;         // groups a K half
+    constexpr int NG = GPH * (BK / 32);
+    auto lds16 = [&](const unsigned char* t, int r, int j) {
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(t + (r * CPR + (j ^ gemm_sw<CPR>(r))) * 16));
+    };
+    bf16x8 bq[BK / 32][NT];
+    bf16x8 aq[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 4 * h + g;  // the lane's 16-byte chunk of the 128-byte row
-      bf16x8 b[NT];
+    for (int jn = 0; jn < NT; ++jn) bq[0][jn] = lds16(sb, wn0 + 16 * jn + fr, g);
 #pragma unroll
-      for (int jn = 0; jn < NT; ++jn) {
-        const int r = wn0 + 16 * jn + fr;
-        b[jn] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + (r * 8 + (j ^ (r & 7))) * 16));
+    for (int u = 0; u < 2; ++u) aq[0][u] = lds16(sa, wm0 + 16 * u + fr, g);
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+      const int h = n / GPH, i = 2 * (n % GPH);
+      if (n + 1 < NG) {
+        const int h1 = (n + 1) / GPH, i1 = 2 * ((n + 1) % GPH);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) aq[(n + 1) & 1][u] = lds16(sa, wm0 + 16 * (i1 + u) + fr, 4 * h1 + g);
       }
-      // A fragments two at a time next to their MFMAs: beside the
-      // accumulators only the B fragments and two A fragments are live
+      if (BK / 32 > 1 && n == 0) {
+        // the second K half's B fragments, well ahead of their first use
 #pragma unroll
-      for (int i = 0; i < MT; i += 2) {
-        bf16x8 a[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = wm0 + 16 * (i + u) + fr;
-          a[u] = as_bf16x8(*reinterpret_cast<const u32x4*>(sa + (r * 8 + (j ^ (r & 7))) * 16));
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int jn = 0; jn < NT; ++jn)
-            acc[i + u][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[jn], a[u], acc[i + u][jn], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int jn = 0; jn < NT; ++jn) bq[BK / 32 - 1][jn] = lds16(sb, wn0 + 16 * jn + fr, 4 + g);
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int jn = 0; jn < NT; ++jn)
+          acc[i + u][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[h][jn], aq[n & 1][u], acc[i + u][jn], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -599,8 +631,11 @@ __global__ __launch_bounds__(64 * kXaWaves) void kg_xattn_kernel(AttnParams p) {
 // 1e-5, biased variance): writes the float32 result (the residual stream)
 // and its bfloat16 copy. With R > 0 the bfloat16 rows go to the two-plane
 // output instead: compact row m (crop cmap[m], slot smap[m]) lands in row
-// (slot / R) * B + b, slot % R of plane-major [2, B, R, C].
+// (slot / R) * B + b, slot % R of plane-major [2, B, R, C]. The row is read
+// once, 16 bytes a lane, and kept in registers (V float4 a lane: C <= 256 V;
+// wider rows take V = 0, three passes over the row).
 // ---------------------------------------------------------------------------
+template <int V>
 __global__ __launch_bounds__(256) void kg_layernorm_kernel(const float* y, const uint16_t* w,
                                                            const uint16_t* bvec, const int* m_dev,
                                                            int C, int B, int R, const int* cmap,
@@ -609,29 +644,66 @@ __global__ __launch_bounds__(256) void kg_layernorm_kernel(const float* y, const
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= *m_dev) return;
-  const float* row = y + (long long)m * C;
-  float s = 0.f;
-  for (int c = lane; c < C; c += 64) s += row[c];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
-  const float mu = s / (float)C;
-  float v = 0.f;
-  for (int c = lane; c < C; c += 64) {
-    const float t = row[c] - mu;
-    v = fmaf(t, t, v);
-  }
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d);
-  const float rs = 1.f / sqrtf(v / (float)C + 1e-5f);
+  const int n4 = C / 4;
+  const f32x4* row = reinterpret_cast<const f32x4*>(y + (long long)m * C);
   long long drow = m;
   if (R > 0) {
     const int b = cmap[m], sl = smap[m];
     drow = ((long long)(sl >= R) * B + b) * R + (sl >= R ? sl - R : sl);
   }
-  for (int c = lane; c < C; c += 64) {
-    const float o = fmaf((row[c] - mu) * rs, bf(w, c), bf(bvec, c));
-    if (x) x[(long long)m * C + c] = o;
-    xb[drow * C + c] = f32_to_bf16_bits(o);
+  auto hsum = [](f32x4 v) { return (v[0] + v[1]) + (v[2] + v[3]); };
+  auto wave_sum = [](float t) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) t += __shfl_xor(t, d);
+    return t;
+  };
+  auto emit = [&](int c4, f32x4 v, float mu, float rs) {
+    const u32x2 wv = *reinterpret_cast<const u32x2*>(w + 4 * c4);
+    const u32x2 bv = *reinterpret_cast<const u32x2*>(bvec + 4 * c4);
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t ww = wv[e >> 1] >> (16 * (e & 1)), bb = bv[e >> 1] >> (16 * (e & 1));
+      o[e] = fmaf((v[e] - mu) * rs, bf16_bits_to_f32((uint16_t)ww), bf16_bits_to_f32((uint16_t)bb));
+    }
+    if (x) reinterpret_cast<f32x4*>(x + (long long)m * C)[c4] = o;
+    const uint32_t lo = f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
+    *reinterpret_cast<u32x2*>(xb + drow * C + 4 * c4) = u32x2{lo, hi};
+  };
+  if constexpr (V > 0) {
+    f32x4 v[V];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int c4 = lane + 64 * i;
+      v[i] = c4 < n4 ? row[c4] : f32x4{0.f, 0.f, 0.f, 0.f};
+      s += hsum(v[i]);
+    }
+    const float mu = wave_sum(s) / (float)C;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (lane + 64 * i < n4) {
+        const f32x4 t = v[i] - mu;
+        q += hsum(t * t);
+      }
+    }
+    const float rs = 1.f / sqrtf(wave_sum(q) / (float)C + 1e-5f);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (lane + 64 * i < n4) emit(lane + 64 * i, v[i], mu, rs);
+  } else {
+    float s = 0.f;
+    for (int c4 = lane; c4 < n4; c4 += 64) s += hsum(row[c4]);
+    const float mu = wave_sum(s) / (float)C;
+    float q = 0.f;
+    for (int c4 = lane; c4 < n4; c4 += 64) {
+      const f32x4 t = row[c4] - mu;
+      q += hsum(t * t);
+    }
+    const float rs = 1.f / sqrtf(wave_sum(q) / (float)C + 1e-5f);
+    for (int c4 = lane; c4 < n4; c4 += 64) emit(c4, row[c4], mu, rs);
   }
 }
 
@@ -639,22 +711,28 @@ __global__ __launch_bounds__(256) void kg_layernorm_kernel(const float* y, const
 // 2 n_b compact rows off[b] .. off[b+1] - 1, the visual slots (slot r) of
 // those rows in row order, then their text slots (slot R + r); cmap and
 // smap give each compact row's crop and slot, off[B] the row count. One
-// workgroup; crops in chunks of 1024 with a running carry.
+// workgroup of 16 waves: per-crop counts by wave ballots (kept in off[]),
+// an exclusive scan over crops in chunks of 1024 with a running carry,
+// then each wave lists its crops' rows in order (ballot prefix counts).
 __global__ __launch_bounds__(1024) void kg_compact_kernel(const uint8_t* mv, const uint8_t* mt,
                                                           int B, int R, int* off, int* cmap,
                                                           int* smap) {
   __shared__ int s_scan[1024];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto prompted = [&](int b, int r) {
+    const long long o = (long long)b * R + r;
+    return r < R && ((mv && mv[o]) || (mt && mt[o]));
+  };
+  for (int b = wave; b < B; b += 16) {
+    int n = 0;
+    for (int r0 = 0; r0 < R; r0 += 64) n += __popcll(__ballot(prompted(b, r0 + lane)));
+    if (lane == 0) off[b] = n;
+  }
+  __syncthreads();  // counts in off[] (workgroup-visible)
   int carry = 0;
   for (int b0 = 0; b0 < B; b0 += 1024) {
     const int b = b0 + tid;
-    auto prompted = [&](int r) {
-      const long long o = (long long)b * R + r;
-      return (mv && mv[o]) || (mt && mt[o]);
-    };
-    int n = 0;
-    if (b < B)
-      for (int r = 0; r < R; ++r) n += prompted(r) ? 1 : 0;
+    const int n = b < B ? off[b] : 0;
     s_scan[tid] = n;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {
@@ -663,44 +741,63 @@ __global__ __launch_bounds__(1024) void kg_compact_kernel(const uint8_t* mv, con
       s_scan[tid] += add;
       __syncthreads();
     }
-    const int start = 2 * (carry + s_scan[tid] - n);
-    if (b < B) {
-      off[b] = start;
-      int j = 0;
-      for (int r = 0; r < R; ++r) {
-        if (!prompted(r)) continue;
-        cmap[start + j] = b;
-        smap[start + j] = r;
-        cmap[start + n + j] = b;
-        smap[start + n + j] = R + r;
-        ++j;
-      }
-    }
+    if (b < B) off[b] = 2 * (carry + s_scan[tid] - n);
     carry += s_scan[1023];
     __syncthreads();  // s_scan is rewritten by the next chunk
   }
   if (tid == 0) off[B] = 2 * carry;
+  __syncthreads();  // starts in off[]
+  for (int b = wave; b < B; b += 16) {
+    const int start = off[b], n = (off[b + 1] - start) / 2;
+    int j = 0;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int r = r0 + lane;
+      const bool pr = prompted(b, r);
+      const unsigned long long msk = __ballot(pr);
+      if (pr) {
+        const int k = start + j + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+        cmap[k] = b;
+        smap[k] = r;
+        cmap[k + n] = b;
+        smap[k + n] = R + r;
+      }
+      j += __popcll(msk);
+    }
+  }
 }
 
-// The compact input rows: slot r < R of crop b holds its visual prototype
-// (slot R + r its text prototype), or the mask token where the row has no
-// prompt of that kind.
-__global__ void kg_assemble_kernel(const uint16_t* vis, const uint8_t* mv, const uint16_t* txt,
-                                   const uint8_t* mt, const uint16_t* tok, int R, int C,
-                                   const int* m_dev, const int* cmap, const int* smap, float* x,
-                                   uint16_t* xb) {
-  const long long n = (long long)(*m_dev) * C;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (long long)gridDim.x * blockDim.x) {
-    const int c = (int)(i % C);
-    const long long m = i / C;
-    const int b = cmap[m], sl = smap[m];
-    const int r = sl < R ? sl : sl - R;
-    const long long row = (long long)b * R + r;
-    const bool have = sl < R ? (mv && mv[row]) : (mt && mt[row]);
-    const uint16_t h = have ? (sl < R ? vis : txt)[row * C + c] : tok[c];
-    x[i] = bf16_bits_to_f32(h);
-    xb[i] = h;
+// The compact input rows, one wave a row: slot r < R of crop b holds its
+// visual prototype (slot R + r its text prototype), or the mask token where
+// the row has no prompt of that kind; 16 bytes (8 channels) a lane.
+__global__ __launch_bounds__(256) void kg_assemble_kernel(const uint16_t* vis, const uint8_t* mv,
+                                                          const uint16_t* txt, const uint8_t* mt,
+                                                          const uint16_t* tok, int R, int C,
+                                                          const int* m_dev, const int* cmap,
+                                                          const int* smap, float* x,
+                                                          uint16_t* xb) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= *m_dev) return;
+  const int b = cmap[m], sl = smap[m];
+  const int r = sl < R ? sl : sl - R;
+  const long long row = (long long)b * R + r;
+  const bool have = sl < R ? (mv && mv[row]) : (mt && mt[row]);
+  const uint16_t* src = have ? (sl < R ? vis : txt) + row * C : tok;
+  for (int c8 = lane; c8 < C / 8; c8 += 64) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(src)[c8];
+    reinterpret_cast<u32x4*>(xb + (long long)m * C)[c8] = v;
+    f32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      lo[2 * e] = bf16_bits_to_f32((uint16_t)(v[e] & 0xffffu));
+      lo[2 * e + 1] = bf16_bits_to_f32((uint16_t)(v[e] >> 16));
+      hi[2 * e] = bf16_bits_to_f32((uint16_t)(v[e + 2] & 0xffffu));
+      hi[2 * e + 1] = bf16_bits_to_f32((uint16_t)(v[e + 2] >> 16));
+    }
+    f32x4* xr = reinterpret_cast<f32x4*>(x + (long long)m * C) + 2 * c8;
+    xr[0] = lo;
+    xr[1] = hi;
   }
 }
 
@@ -765,10 +862,12 @@ hipError_t gemm(const uint16_t* A, long long a_bstride, int a_rows, int lda, con
   // the wide tile where N fills it, else 128 columns
   if (N % 256 == 0) {
     const int tiles = ((M + kGM - 1) / kGM) * (N / 256);
-    hipLaunchKernelGGL(kg_gemm_kernel<256>, dim3(tiles), dim3(512), 2 * gemm_stage_bytes<256>(), st, p);
+    hipLaunchKernelGGL((kg_gemm_kernel<256, kGemmBK, kGemmNS>), dim3(tiles), dim3(512),
+                       (gemm_lds_bytes<256, kGemmBK, kGemmNS>()), st, p);
   } else {
     const int tiles = ((M + kGM - 1) / kGM) * ((N + 127) / 128);
-    hipLaunchKernelGGL(kg_gemm_kernel<128>, dim3(tiles), dim3(512), 2 * gemm_stage_bytes<128>(), st, p);
+    hipLaunchKernelGGL((kg_gemm_kernel<128, kGemmBK, kGemmNS>), dim3(tiles), dim3(512),
+                       (gemm_lds_bytes<128, kGemmBK, kGemmNS>()), st, p);
   }
   return hipGetLastError();
 }
@@ -790,8 +889,15 @@ hipError_t attn(const AttnParams& p, int B, int tk_max, hipStream_t st) {
 hipError_t layernorm(const float* y, const uint16_t* w, const uint16_t* b, int M,
                      const int* m_dev, int C, int B, int R, const int* cmap, const int* smap,
                      float* x, uint16_t* xb, hipStream_t st) {
-  hipLaunchKernelGGL(kg_layernorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, y, w, b, m_dev, C,
-                     B, R, cmap, smap, x, xb);
+  if (C <= 1024)
+    hipLaunchKernelGGL(kg_layernorm_kernel<4>, dim3((M + 3) / 4), dim3(256), 0, st, y, w, b, m_dev,
+                       C, B, R, cmap, smap, x, xb);
+  else if (C <= 2048)
+    hipLaunchKernelGGL(kg_layernorm_kernel<8>, dim3((M + 3) / 4), dim3(256), 0, st, y, w, b, m_dev,
+                       C, B, R, cmap, smap, x, xb);
+  else
+    hipLaunchKernelGGL(kg_layernorm_kernel<0>, dim3((M + 3) / 4), dim3(256), 0, st, y, w, b, m_dev,
+                       C, B, R, cmap, smap, x, xb);
   return hipGetLastError();
 }
 
@@ -815,9 +921,7 @@ hipError_t launch_kg(const KgArgs& a, hipStream_t st) {
                      w.cmap, w.smap);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   {
-    const long long n = (long long)M * C;
-    const int grid = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
-    hipLaunchKernelGGL(kg_assemble_kernel, dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL(kg_assemble_kernel, dim3((M + 3) / 4), dim3(256), 0, st,
                        static_cast<const uint16_t*>(a.vis), a.mv, static_cast<const uint16_t*>(a.txt),
                        a.mt, tok, R, C, mc, w.cmap, w.smap, w.x, w.xb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
