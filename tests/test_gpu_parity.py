@@ -464,6 +464,8 @@ def test_bf16_heatmap_output_longtail(gkd):
 
 @pytest.mark.parametrize("shape,p_valid", [
     ((3, 48, 9, 8, 30), 0.6),      # H not a multiple of the row-ring depth; C < one block
+    ((5, 272, 12, 8, 30), 0.6),    # H a multiple of the ring depth: the ring runs on into
+                                   #   the next item (two channel blocks, the second partial)
     ((2, 32, 5, 16, 12), 0.7),     # short maps, no cross-item prefetch
     ((2, 16, 1, 8, 5), 1.0),       # a one-row map
     ((2, 144, 8, 16, 10), 0.5),    # a partial channel block (one wave of eight)
