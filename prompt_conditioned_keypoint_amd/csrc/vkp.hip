@@ -232,33 +232,22 @@ __global__ __launch_bounds__(kVThreads) void vkp_kernel(VkParams p) {
 // of item k already fetch the first image rows of the next one, so the
 // row selection and weight set-up between items overlap the HBM stream.
 // ---------------------------------------------------------------------------
-// Channel-row maps (TOK false): 16 waves, one workgroup per CU, image rows
-// streamed into a per-wave LDS ring kFRing rows deep by direct-to-LDS
-// loads. Token maps (TOK true): 8 waves, two workgroups per CU, a register
-// ring kFDepth rows deep (each row passes through LDS for a transpose).
-// Either way 4 waves share a SIMD.
-template <bool TOK>
-constexpr int fwaves() { return TOK ? 8 : 16; }
-template <bool TOK>
-constexpr int fthreads() { return fwaves<TOK>() * kWave; }
-template <bool TOK>
-constexpr int fch() { return fwaves<TOK>() * 16; }  // channels per item
-template <bool TOK>
-constexpr int fwg_per_cu() { return TOK ? 2 : 1; }
+constexpr int kFWaves = 8;
+constexpr int kFThreads = kFWaves * kWave;  // 512
 constexpr int kFRows = 80;                  // valid rows per item
 constexpr int kFMaxHW = 32;                 // H, W <= 32 (one half wave per weight row)
-constexpr int kFDepth = 4;                  // TOK: image rows loaded ahead per wave (registers)
-constexpr int kFRing = 6;                   // channel rows: image rows loaded ahead per wave (LDS)
+constexpr int kFCh = kFWaves * 16;          // channels per item
+constexpr int kFDepth = 4;                  // image rows loaded ahead per wave
 constexpr int kFMaxR = 256;                 // R <= 256 (masks and keypoints staged in LDS)
 constexpr int kFList = 4096;                // (crop, row block) pairs per launch
-constexpr size_t kFRingLds = (size_t)16 * kFRing * 1024;  // dynamic LDS of a channel-row workgroup
+constexpr int kFWgPerCu = 2;                // resident workgroups per CU (4 waves per SIMD)
 
 struct VkFastParams {
   const uint16_t* support;
   const float* kpts;
   const uint8_t* valid;
   int B, C, H, W, R, S;
-  bool chain;  // H a multiple of the ring depth: the ring runs on into the next item
+  bool chain;  // H % kFDepth == 0: the ring runs on into the next item
   float stride, inv_stride;
   float nl2s2;      // -log2(e) / (2 sigma^2): w = 2^(d^2 nl2s2)
   int cblocks;
@@ -344,38 +333,17 @@ __device__ __forceinline__ u32x4 load_row(const char* base, uint32_t loff) {
   return *reinterpret_cast<const u32x4*>(base + loff);
 }
 
-typedef __attribute__((address_space(3))) void vk_lds_void;
-typedef __attribute__((address_space(1))) void vk_glb_void;
-
-// One image row of the wave's 16 channels straight into LDS slot `slot`
-// (1 KiB: lane l's 16 bytes at 16 l, the lane order of load_row).
-__device__ __forceinline__ void dma_row(const char* base, uint32_t loff, unsigned char* slot) {
-  __builtin_amdgcn_global_load_lds((vk_glb_void*)(base + loff), (vk_lds_void*)slot, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone
-template <int N>
-__device__ __forceinline__ void vk_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  // gfx9 layout: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Streams one item through the ring and writes its prototypes. The ring (D
-// = kFDepth registers for TOK, D = kFRing LDS slots of the wave's lring
-// otherwise) enters holding rows 0 .. D-1 of this item (slot = row mod D)
-// and, when nsrc is set (H a multiple of D), leaves holding rows 0 .. D-1
-// of the next item: the refill of slot d in the last period is exactly the
-// next item's row d. Without nsrc the tail refills re-read the last row and
-// the caller loads the next ring itself. The LDS ring refills every slot it
-// consumes (a row is in place once at most D - 1 later loads are in
-// flight), so the load count the waits rely on never changes.
+// Streams one item through the ring and writes its prototypes. The ring
+// enters holding rows 0 .. kFDepth-1 of this item (slot = row mod kFDepth)
+// and, when nsrc is set (H a multiple of kFDepth), leaves holding rows
+// 0 .. kFDepth-1 of the next item: the refill of slot d in the last period
+// is exactly the next item's row d. Without nsrc the tail refills re-read
+// the last row and the caller loads the next ring itself.
 template <int MT, bool TOK>
 __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int c0, int nsel,
                                               const char* src, uint32_t loff,
                                               bool col_ok, const char* nsrc,
                                               u32x4 (&ring)[kFDepth],
-                                              unsigned char* lring,
                                               const int* s_rows,
                                               const uint16_t (*s_wxh)[kFMaxHW],
                                               const uint16_t (*s_wxl)[kFMaxHW],
@@ -397,76 +365,48 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
 #pragma unroll
   for (int h = 0; h < MT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (TOK) {
-    for (int i0 = 0; i0 < p.H; i0 += kFDepth) {
+  for (int i0 = 0; i0 < p.H; i0 += kFDepth) {
 #pragma unroll
-      for (int d = 0; d < kFDepth; ++d) {
-        const int i = i0 + d;
-        if (i < p.H) {
-          const u32x4 v = col_ok ? ring[d] : u32x4{0u, 0u, 0u, 0u};
-          const int ni = i + kFDepth;
-          const size_t rowb = TOK ? (size_t)p.W * p.C * 2 : (size_t)p.W * 2;
-          const char* a = ni < p.H ? src + ni * rowb
-                          : nsrc   ? nsrc + (ni - p.H) * rowb
-                                   : src + (p.H - 1) * rowb;
-          ring[d] = load_row(a, loff);
-          bf16x8 bv;
-          if constexpr (TOK) {
-            // pixel j = lane / 2 of the row, channels 8 (lane % 2) .. + 7, to the
-            // slice; back as pixels 8 g4 .. 8 g4 + 7 of channel n16 (rows
-            // 8 g4 + n16 / 4 and + 4, columns 4 (n16 % 4) .. + 3)
-            *reinterpret_cast<u32x4*>(tok_slice + (lane >> 1) * kFTokRow + 16 * (lane & 1)) = v;
-            const uint32_t lo_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
-                tok_slice + (8 * g4 + (n16 >> 2)) * kFTokRow + 8 * (n16 & 3));
-            u32x2 lo, hi;
-            asm volatile(
-                "ds_read_b64_tr_b16 %0, %2\n"
-                "ds_read_b64_tr_b16 %1, %2 offset:%3\n"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(lo), "=&v"(hi)
-                : "v"(lo_addr), "i"(4 * kFTokRow)
-                : "memory");
-            bv = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-          } else {
-            bv = __builtin_bit_cast(bf16x8, v);
-          }
+    for (int d = 0; d < kFDepth; ++d) {
+      const int i = i0 + d;
+      if (i < p.H) {
+        const u32x4 v = col_ok ? ring[d] : u32x4{0u, 0u, 0u, 0u};
+        const int ni = i + kFDepth;
+        const size_t rowb = TOK ? (size_t)p.W * p.C * 2 : (size_t)p.W * 2;
+        const char* a = ni < p.H ? src + ni * rowb
+                        : nsrc   ? nsrc + (ni - p.H) * rowb
+                                 : src + (p.H - 1) * rowb;
+        ring[d] = load_row(a, loff);
+        bf16x8 bv;
+        if constexpr (TOK) {
+          // pixel j = lane / 2 of the row, channels 8 (lane % 2) .. + 7, to the
+          // slice; back as pixels 8 g4 .. 8 g4 + 7 of channel n16 (rows
+          // 8 g4 + n16 / 4 and + 4, columns 4 (n16 % 4) .. + 3)
+          *reinterpret_cast<u32x4*>(tok_slice + (lane >> 1) * kFTokRow + 16 * (lane & 1)) = v;
+          const uint32_t lo_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
+              tok_slice + (8 * g4 + (n16 >> 2)) * kFTokRow + 8 * (n16 & 3));
+          u32x2 lo, hi;
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %2\n"
+              "ds_read_b64_tr_b16 %1, %2 offset:%3\n"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(lo), "=&v"(hi)
+              : "v"(lo_addr), "i"(4 * kFTokRow)
+              : "memory");
+          bv = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        } else {
+          bv = __builtin_bit_cast(bf16x8, v);
+        }
 #pragma unroll
-          for (int h = 0; h < MT; ++h) {
-            f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[h], bv, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                              0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[h], bv, t, 0, 0, 0);
-            const f32x4 wy = *reinterpret_cast<const f32x4*>(&s_wy[i][16 * h + 4 * g4]);
+        for (int h = 0; h < MT; ++h) {
+          f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[h], bv, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[h], bv, t, 0, 0, 0);
+          const f32x4 wy = *reinterpret_cast<const f32x4*>(&s_wy[i][16 * h + 4 * g4]);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(wy[k], t[k], acc[h][k]);
-          }
+          for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(wy[k], t[k], acc[h][k]);
         }
       }
-    }
-  } else {
-    const size_t rowb = (size_t)p.W * 2;
-    int slot = 0;
-    for (int i = 0; i < p.H; ++i) {
-      vk_wait_vmcnt<kFRing - 1>();  // row i landed; the D - 1 rows after it may fly
-      unsigned char* sl = lring + slot * 1024;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(sl + 16 * lane);
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, col_ok ? raw : u32x4{0u, 0u, 0u, 0u});
-      // the slot's read is complete before its refill is issued
-      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-      const int ni = i + kFRing;
-      const char* a = ni < p.H ? src + ni * rowb
-                      : nsrc   ? nsrc + (ni - p.H) * rowb
-                               : src + (p.H - 1) * rowb;
-      dma_row(a, loff, sl);
-#pragma unroll
-      for (int h = 0; h < MT; ++h) {
-        f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[h], bv, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                          0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[h], bv, t, 0, 0, 0);
-        const f32x4 wy = *reinterpret_cast<const f32x4*>(&s_wy[i][16 * h + 4 * g4]);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[h][k] = fmaf(wy[k], t[k], acc[h][k]);
-      }
-      slot = slot + 1 == kFRing ? 0 : slot + 1;
     }
   }
   // D layout: lane (n16, g4) holds rows 16 h + 4 g4 + k of channel c0 + n16
@@ -483,11 +423,7 @@ __device__ __forceinline__ void vkp_fast_item(const VkFastParams& p, int b, int 
 }
 
 template <bool TOK>
-__global__ __launch_bounds__(fthreads<TOK>(), fwg_per_cu<TOK>() * fwaves<TOK>() / 4) void vkp_fast_kernel(VkFastParams p) {
-  constexpr int kFWaves = fwaves<TOK>();
-  constexpr int kFThreads = fthreads<TOK>();
-  constexpr int kFCh = fch<TOK>();
-  extern __shared__ __align__(16) unsigned char s_ring[];  // channel rows: kFRing KiB a wave
+__global__ __launch_bounds__(kFThreads, kFWgPerCu * kFWaves / 4) void vkp_fast_kernel(VkFastParams p) {
   __shared__ __align__(16) unsigned char s_tok[TOK ? kFWaves * 32 * kFTokRow : 16];
   __shared__ int s_list[kFList];  // crop << 2 | row block
   __shared__ int s_wsum[kFWaves];
@@ -527,13 +463,8 @@ __global__ __launch_bounds__(fthreads<TOK>(), fwg_per_cu<TOK>() * fwaves<TOK>() 
     for (int j = 0; j < nb; ++j) s_list[first + j] = (bb << 2) | j;
     lds_sync();
   }
-  // each workgroup takes a contiguous run of items, so consecutive items
-  // are mostly channel blocks of one crop and row block, which share the
-  // selected rows and weights (set up once) and keep the ring streaming
   const int nitems = nlist * p.cblocks;
-  const int per = (nitems + (int)gridDim.x - 1) / (int)gridDim.x;
-  int k = blockIdx.x * per;
-  const int kend = min(k + per, nitems);
+  int k = blockIdx.x;
   if (k >= nitems) return;
 
   const int g4 = lane >> 4;
@@ -556,15 +487,7 @@ __global__ __launch_bounds__(fthreads<TOK>(), fwg_per_cu<TOK>() * fwaves<TOK>() 
           : (uint32_t)(((lane & 15) * p.S + (col_ok ? 8 * g4 : 0)) * 2);
   const bool row_ok = TOK ? tok_ok : col_ok;
   unsigned char* const tok_slice = s_tok + (TOK ? (size_t)wave * 32 * kFTokRow : 0);
-  unsigned char* const lring = s_ring + (TOK ? 0 : (size_t)wave * kFRing * 1024);
   const char* src = item_base<TOK>(p, b, on ? c0 : 0);
-  // the first D rows of an item (rows past H repeat its last row, so every
-  // fill issues D loads)
-  auto fill_lds = [&](const char* base) {
-#pragma unroll
-    for (int d = 0; d < kFRing; ++d)
-      dma_row(base + (size_t)(d < p.H ? d : p.H - 1) * p.W * 2, loff, lring + d * 1024);
-  };
 
   // masks and keypoints of the item's crop (registers until staged)
   uint8_t mv = 0;
@@ -577,81 +500,71 @@ __global__ __launch_bounds__(fthreads<TOK>(), fwg_per_cu<TOK>() * fwaves<TOK>() 
   }
   u32x4 ring[kFDepth];
 #pragma unroll
-  for (int d = 0; d < kFDepth; ++d) ring[d] = u32x4{0u, 0u, 0u, 0u};
-  if constexpr (TOK) {
-#pragma unroll
-    for (int d = 0; d < kFDepth; ++d)
-      if (on && d < p.H) ring[d] = load_row(src + (size_t)d * p.W * p.C * 2, loff);
-  } else {
-    if (on) fill_lds(src);
+  for (int d = 0; d < kFDepth; ++d) {
+    ring[d] = u32x4{0u, 0u, 0u, 0u};
+    if (on && d < p.H) ring[d] = load_row(src + (size_t)d * (TOK ? p.W * p.C : p.W) * 2, loff);
   }
 
-  bool setup = true;  // the item's crop or row block differs from the last one's
-  int nsel = 0;
   for (;;) {
-    if (setup) {
-      // stage the crop's masks and keypoints, pick the item's rows
-      if (tid < p.R) {
-        s_valid[tid] = mv;
-        s_kx[tid] = mx;
-        s_ky[tid] = my;
-      }
-      lds_sync();
-      if (wave == 0)
-        select_rows(s_valid, nullptr, p.R, lane, rblk, kFRows, s_rows, s_dummy0, s_dummy1,
-                    &s_nvalid, &s_nsel);
-      lds_sync();
-      nsel = s_nsel;
-      // separable weight factors, each relative to the nearest cell centre,
-      // for the M tiles the MFMAs read (rows past nsel, and columns past
-      // W / H, get weight 0)
-      const int rows16 = (nsel + 15) / 16 * 16;
-#pragma nounroll
-      for (int q = tid; q < rows16 * kFMaxHW; q += kFThreads) {
-        const int m = q / kFMaxHW, j = q - m * kFMaxHW;
-        float wx = 0.f, wy = 0.f;
-        if (m < nsel) {
-          const int r = s_rows[m];
-          if (j < p.W) {
-            const float x = s_kx[r];
-            const float dx0 = centre_offset_fast(x, p.stride, p.inv_stride, p.W);
-            const float d = ((float)j + 0.5f) * p.stride - x;
-            wx = __builtin_amdgcn_exp2f((d * d - dx0 * dx0) * p.nl2s2);
-          }
-          if (j < p.H) {
-            const float y = s_ky[r];
-            const float dy0 = centre_offset_fast(y, p.stride, p.inv_stride, p.H);
-            const float d = ((float)j + 0.5f) * p.stride - y;
-            wy = __builtin_amdgcn_exp2f((d * d - dy0 * dy0) * p.nl2s2);
-          }
-        }
-        const uint16_t hi = f32_to_bf16_bits(wx);
-        const uint16_t lo = f32_to_bf16_bits(wx - bf16_bits_to_f32(hi));
-        s_wxh[m][j] = hi;
-        s_wxl[m][j] = lo;
-        s_wy[j][m] = wy;
-        // normaliser: sum_ij wy(i) wx(j) = (sum_i wy)(sum_j wx), with wx as
-        // the hi + lo parts the MFMA sees; the 32 lanes of row m (a half
-        // wave: kFMaxHW = 32 and q steps by whole waves) sum in registers
-        const float sx = half_wave_sum(bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo));
-        const float sy = half_wave_sum(wy);
-        if (j == kFMaxHW - 1 && m < nsel) s_inv[m] = 1.f / (sx * sy);
-      }
-      lds_sync();
+    // stage the crop's masks and keypoints, pick the item's rows
+    if (tid < p.R) {
+      s_valid[tid] = mv;
+      s_kx[tid] = mx;
+      s_ky[tid] = my;
     }
+    lds_sync();
+    if (wave == 0)
+      select_rows(s_valid, nullptr, p.R, lane, rblk, kFRows, s_rows, s_dummy0, s_dummy1,
+                  &s_nvalid, &s_nsel);
+    lds_sync();
+    const int nsel = s_nsel;
+    // separable weight factors, each relative to the nearest cell centre,
+    // for the M tiles the MFMAs read (rows past nsel, and columns past
+    // W / H, get weight 0)
+    const int rows16 = (nsel + 15) / 16 * 16;
+#pragma nounroll
+    for (int q = tid; q < rows16 * kFMaxHW; q += kFThreads) {
+      const int m = q / kFMaxHW, j = q - m * kFMaxHW;
+      float wx = 0.f, wy = 0.f;
+      if (m < nsel) {
+        const int r = s_rows[m];
+        if (j < p.W) {
+          const float x = s_kx[r];
+          const float dx0 = centre_offset_fast(x, p.stride, p.inv_stride, p.W);
+          const float d = ((float)j + 0.5f) * p.stride - x;
+          wx = __builtin_amdgcn_exp2f((d * d - dx0 * dx0) * p.nl2s2);
+        }
+        if (j < p.H) {
+          const float y = s_ky[r];
+          const float dy0 = centre_offset_fast(y, p.stride, p.inv_stride, p.H);
+          const float d = ((float)j + 0.5f) * p.stride - y;
+          wy = __builtin_amdgcn_exp2f((d * d - dy0 * dy0) * p.nl2s2);
+        }
+      }
+      const uint16_t hi = f32_to_bf16_bits(wx);
+      const uint16_t lo = f32_to_bf16_bits(wx - bf16_bits_to_f32(hi));
+      s_wxh[m][j] = hi;
+      s_wxl[m][j] = lo;
+      s_wy[j][m] = wy;
+      // normaliser: sum_ij wy(i) wx(j) = (sum_i wy)(sum_j wx), with wx as
+      // the hi + lo parts the MFMA sees; the 32 lanes of row m (a half
+      // wave: kFMaxHW = 32 and q steps by whole waves) sum in registers
+      const float sx = half_wave_sum(bf16_bits_to_f32(hi) + bf16_bits_to_f32(lo));
+      const float sy = half_wave_sum(wy);
+      if (j == kFMaxHW - 1 && m < nsel) s_inv[m] = 1.f / (sx * sy);
+    }
+    lds_sync();
 
-    // the next item: its masks and keypoints are requested now (a new crop
-    // or row block only), its first rows by the last refills of this
-    // item's ring
-    const int kn = k + 1;
-    const bool has_next = kn < kend;
+    // the next item: its masks and keypoints are requested now, its first
+    // rows by the last refills of this item's ring
+    const int kn = k + (int)gridDim.x;
+    const bool has_next = kn < nitems;
     int bn = 0, rn = 0, cn = 0;
     if (has_next) decode(kn, bn, rn, cn);
     const bool on_n = has_next && cn < p.C;
     const char* nsrc_all = on_n ? item_base<TOK>(p, bn, cn) : nullptr;
     const char* nsrc = p.chain ? nsrc_all : nullptr;
-    const bool same = has_next && bn == b && rn == rblk;
-    if (has_next && !same && tid < p.R) {
+    if (has_next && tid < p.R) {
       const size_t o = (size_t)bn * p.R + tid;
       mv = p.valid[o];
       mx = p.kpts[2 * o];
@@ -659,22 +572,17 @@ __global__ __launch_bounds__(fthreads<TOK>(), fwg_per_cu<TOK>() * fwaves<TOK>() 
     }
     if (on) {
       switch ((nsel + 15) / 16) {
-        case 1: vkp_fast_item<1, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, lring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
-        case 2: vkp_fast_item<2, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, lring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
-        case 3: vkp_fast_item<3, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, lring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
-        case 4: vkp_fast_item<4, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, lring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
-        default: vkp_fast_item<5, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, lring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 1: vkp_fast_item<1, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 2: vkp_fast_item<2, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 3: vkp_fast_item<3, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        case 4: vkp_fast_item<4, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
+        default: vkp_fast_item<5, TOK>(p, b, c0, nsel, src, loff, row_ok, nsrc, ring, s_rows, s_wxh, s_wxl, s_wy, s_inv, lane, tok_slice); break;
       }
     }
     if (on_n && !(on && p.chain)) {
-      if constexpr (TOK) {
 #pragma unroll
-        for (int d = 0; d < kFDepth; ++d)
-          if (d < p.H) ring[d] = load_row(nsrc_all + (size_t)d * p.W * p.C * 2, loff);
-      } else {
-        vk_wait_vmcnt<0>();  // this item's tail refills land before the slots are refilled
-        fill_lds(nsrc_all);
-      }
+      for (int d = 0; d < kFDepth; ++d)
+        if (d < p.H) ring[d] = load_row(nsrc_all + (size_t)d * (TOK ? p.W * p.C : p.W) * 2, loff);
     }
     if (!has_next) break;
     k = kn;
@@ -683,10 +591,9 @@ __global__ __launch_bounds__(fthreads<TOK>(), fwg_per_cu<TOK>() * fwaves<TOK>() 
     c0 = cn;
     on = on_n;
     src = on_n ? nsrc_all : src;
-    setup = !same;
     // every wave is done with this item's rows, weights and normaliser
     // before the next set-up overwrites them
-    if (setup) lds_sync();
+    lds_sync();
   }
 }
 
@@ -707,12 +614,11 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
     f.W = a.W;
     f.R = a.R;
     f.S = a.H * a.W;
-    f.chain = a.H % (a.tokens ? kFDepth : kFRing) == 0;
+    f.chain = a.H % kFDepth == 0;
     f.stride = a.stride;
     f.inv_stride = 1.f / a.stride;
     f.nl2s2 = (float)(-1.4426950408889634 / (2.0 * (double)a.sigma * (double)a.sigma));
-    const int fc = a.tokens ? fch<true>() : fch<false>();
-    f.cblocks = (a.C + fc - 1) / fc;
+    f.cblocks = (a.C + kFCh - 1) / kFCh;
     f.mask_words = a.R % 4 == 0 && (reinterpret_cast<uintptr_t>(a.valid) & 3u) == 0;
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -733,15 +639,12 @@ hipError_t launch_vkp(const VkpArgs& a, hipStream_t stream) {
       f.protos = static_cast<uint16_t*>(a.protos) + rows0 * a.C;
       f.B = nb;
       const long long items = (long long)nb * rblocks * f.cblocks;
-      const long long cap =
-          (long long)(a.tokens ? fwg_per_cu<true>() : fwg_per_cu<false>()) * (cus > 0 ? cus : 1);
+      const long long cap = (long long)kFWgPerCu * (cus > 0 ? cus : 1);
       const int grid = (int)(items < cap ? items : cap);
       if (a.tokens)
-        hipLaunchKernelGGL(vkp_fast_kernel<true>, dim3((unsigned)grid), dim3(fthreads<true>()), 0,
-                           stream, f);
+        hipLaunchKernelGGL(vkp_fast_kernel<true>, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
       else
-        hipLaunchKernelGGL(vkp_fast_kernel<false>, dim3((unsigned)grid), dim3(fthreads<false>()),
-                           kFRingLds, stream, f);
+        hipLaunchKernelGGL(vkp_fast_kernel<false>, dim3((unsigned)grid), dim3(kFThreads), 0, stream, f);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
