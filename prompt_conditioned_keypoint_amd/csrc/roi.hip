@@ -8,16 +8,19 @@
 // frame. In top-down use every detector box is one ROI. The conventions
 // the card leaves open are fixed in include/gkdhead.h.
 //
-// Preprocess: a workgroup per (box, 1024 quads of 4 output columns). The
-// box geometry is integer arithmetic; the bilinear taps and their
-// fractions come from exact integer division ((2u + 1) * bw - nw over
-// 2 * nw), so a tap never depends on a rounded float, and the column taps
-// are tabulated once per workgroup in LDS. The source image is small next
-// to the output and is served from L2: each output pixel reads its two
-// horizontally adjacent RGB taps of each source row as one 12-byte aligned
-// window (6 bytes at any offset fit in it) instead of twelve byte loads.
-// The output planes take 16-byte (f32) or 8-byte (bf16) non-temporal
-// stores. The kernel is bound by its per-pixel VALU work, not by HBM.
+// Preprocess, direct form (float32 canvases, and bfloat16 ones wider than
+// 2048): a workgroup per (box, 1024 quads of 4 output columns). The box
+// geometry is integer arithmetic; the bilinear taps and their fractions
+// come from exact integer division ((2u + 1) * bw - nw over 2 * nw), so a
+// tap never depends on a rounded float, and the column taps are tabulated
+// once per workgroup in LDS. The source image is small next to the output
+// and is served from L2: each output pixel reads its two horizontally
+// adjacent RGB taps of each source row as one 12-byte aligned window (6
+// bytes at any offset fit in it) instead of twelve byte loads. The output
+// planes take 16-byte (f32) or 8-byte (bf16) non-temporal stores.
+// Separable form (bfloat16 canvases up to 2048): the same values with the
+// horizontal step done once per source row (roi_win_kernel), which removes
+// about half of the per-pixel VALU work that bounds the direct form.
 #include "gkd_device.hpp"
 #include "launch.hpp"
 
@@ -240,6 +243,139 @@ __global__ __launch_bounds__(kRThreads) void roi_kernel(RoiArgs a, RoiNorm nm) {
   }
 }
 
+// Separable form: a thread owns two canvas columns of one box and walks
+// kRRows canvas rows down them, keeping the horizontal interpolation of the
+// two source rows the current canvas row uses (its top and bottom taps) and
+// computing one only when a canvas row moves to a source row it does not
+// hold yet. The values are the direct form's, bit for bit (the same top and
+// bottom, then the same vertical step), with the horizontal work and the
+// image reads done about once per source row instead of twice per canvas
+// row. All threads of a workgroup walk the same rows, so the reuse tests are
+// uniform. A workgroup: one box, kRRows rows, all column pairs (up to
+// kRWinMaxL columns).
+constexpr int kRRows = 8;
+constexpr int kRWinMaxL = 2048;  // 1024 threads of two columns
+
+struct RoiCols {
+  int off[2];    // 3 s0 of the left tap, -1: pad column
+  float lx[2];
+};
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(1024) void roi_win_kernel(RoiArgs a, RoiNorm nm) {
+  const int b = blockIdx.y, v0 = blockIdx.x * kRRows, u0 = 2 * (int)threadIdx.x;
+  const RoiGeom g = roi_geom(a.boxes + 4 * (size_t)b, a.H, a.W, a.L);
+  const int L = a.L;
+  if (u0 >= L) return;  // no barrier below
+  const float rw = 1.f / (float)(2 * g.nw), rh = 1.f / (float)(2 * g.nh);
+  RoiCols cols;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int u = u0 + e;
+    cols.off[e] = -1;
+    cols.lx[e] = 0.f;
+    if (g.bw > 0 && u < L && u >= g.px && u < g.px + g.nw) {
+      int s0, s1;
+      float lx;
+      roi_taps(u - g.px, g.bw, g.nw, rw, s0, s1, lx);
+      // at the right edge both taps are the last pixel: weight 0 on the
+      // second makes the value that pixel's
+      cols.off[e] = 3 * s0;
+      cols.lx[e] = s1 != s0 ? lx : 0.f;
+    }
+  }
+  const uint8_t* __restrict__ img = a.image;
+  const size_t total = (size_t)a.H * a.W * 3;
+  // horizontal interpolation of source row r (in the crop) at this
+  // thread's columns, the three channels
+  auto hrow = [&](int r, float (&h)[3][2]) {
+    const size_t row = ((size_t)(g.y0 + r) * a.W + g.x0) * 3;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      if (cols.off[e] >= 0) {
+        uint32_t lo, hi;
+        load8<false>(img, total, row + (size_t)cols.off[e], lo, hi);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          const float p0 = byte_f(lo, hi, c), p1 = byte_f(lo, hi, 3 + c);
+          h[c][e] = fmaf(cols.lx[e], p1 - p0, p0);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) h[c][e] = 0.f;
+      }
+    }
+  };
+  int ra = -1, rb = -1;  // source rows held in ha and hb
+  float ha[3][2], hb[3][2];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) ha[c][0] = ha[c][1] = hb[c][0] = hb[c][1] = 0.f;
+  const size_t plane = (size_t)L * L;
+  for (int k = 0; k < kRRows; ++k) {
+    const int v = v0 + k;
+    if (v >= L) break;
+    float o[3][2];
+    if (g.bw > 0 && v >= g.py && v < g.py + g.nh) {
+      int r0, r1;
+      float ly;
+      roi_taps(v - g.py, g.bh, g.nh, rh, r0, r1, ly);
+      // (ra, rb) <- (r0, r1), reusing what is held (r0 <= r1 <= r0 + 1, and
+      // both move down with v)
+      if (r0 != ra) {
+        if (r0 == rb) {
+#pragma unroll
+          for (int c = 0; c < 3; ++c) ha[c][0] = hb[c][0], ha[c][1] = hb[c][1];
+        } else {
+          hrow(r0, ha);
+        }
+        ra = r0;
+      }
+      if (r1 != rb) {
+        if (r1 == ra) {
+#pragma unroll
+          for (int c = 0; c < 3; ++c) hb[c][0] = ha[c][0], hb[c][1] = ha[c][1];
+        } else {
+          hrow(r1, hb);
+        }
+        rb = r1;
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+          o[c][e] = cols.off[e] >= 0
+                        ? fmaf(fmaf(ly, hb[c][e] - ha[c][e], ha[c][e]), nm.scale[c], nm.bias[c])
+                        : nm.pad[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 3; ++c) o[c][0] = o[c][1] = nm.pad[c];
+    }
+    const size_t base = (size_t)b * 3 * plane + (size_t)v * L + u0;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      if constexpr (BF16) {
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + base + c * plane;
+        const uint32_t w =
+            __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{o[c][0], o[c][1]}, bf16x2));
+        if constexpr (VEC) {
+          __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(dst));
+        } else {
+          dst[0] = (uint16_t)(w & 0xffffu);
+          if (u0 + 1 < L) dst[1] = (uint16_t)(w >> 16);
+        }
+      } else {
+        float* dst = static_cast<float*>(a.out) + base + c * plane;
+        if constexpr (VEC) {
+          __builtin_nontemporal_store(f32x2{o[c][0], o[c][1]}, reinterpret_cast<f32x2*>(dst));
+        } else {
+          dst[0] = o[c][0];
+          if (u0 + 1 < L) dst[1] = o[c][1];
+        }
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kRThreads) void backproject_kernel(BackprojectArgs a) {
   const size_t i = (size_t)blockIdx.x * kRThreads + threadIdx.x;
   if (i >= (size_t)a.B * a.R) return;
@@ -271,10 +407,22 @@ hipError_t launch_roi(const RoiArgs& a, hipStream_t stream) {
     nm.bias[c] = -kMean[c] / kStd[c];
     nm.pad[c] = fmaf(kPad[c], nm.scale[c], nm.bias[c]);
   }
+  const bool vec = a.L % 4 == 0;
+  // bfloat16 canvases: the separable form (its lower VALU count decides);
+  // float32 ones: the direct form, whose 16-byte stores keep the write
+  // stream at its rate
+  if (a.bf16 && a.L <= kRWinMaxL) {
+    const int threads = ((a.L + 1) / 2 + kWave - 1) / kWave * kWave;
+    const dim3 grid((unsigned)((a.L + kRRows - 1) / kRRows), (unsigned)a.B);
+    if (a.L % 2 == 0)
+      hipLaunchKernelGGL((roi_win_kernel<true, true>), grid, dim3(threads), 0, stream, a, nm);
+    else
+      hipLaunchKernelGGL((roi_win_kernel<true, false>), grid, dim3(threads), 0, stream, a, nm);
+    return hipGetLastError();
+  }
   const long long quads = (long long)a.L * ((a.L + 3) / 4);
   const dim3 grid((unsigned)((quads + kQuadsPerBlock - 1) / kQuadsPerBlock), (unsigned)a.B);
   const size_t lds = (size_t)a.L * sizeof(int2);  // the column table
-  const bool vec = a.L % 4 == 0;
   if (a.bf16) {
     if (vec)
       hipLaunchKernelGGL((roi_kernel<true, true>), grid, dim3(kRThreads), lds, stream, a, nm);

@@ -86,6 +86,25 @@ def test_roi_preprocess_matches_oracle(gkd, ora, dtype, size):
         assert np.mean(g == w16) > 0.99
 
 
+def test_roi_preprocess_bf16_both_forms(gkd, ora):
+    """bfloat16 canvases up to 2048 wide take the separable kernel, wider ones
+    the direct kernel; both against the oracle, with the size-384 edge boxes
+    (up- and downscaled, clamped, one-pixel and empty)."""
+    rng = np.random.default_rng(21)
+    img = rng.integers(0, 256, (300, 500, 3)).astype(np.uint8)
+    boxes = np.array([EDGE_BOXES[i] for i in (0, 1, 4, 5, 7)], np.int32)
+    for size in (2048, 2050):
+        print(f"[roi] bf16 size={size}", flush=True)
+        got = gkd.roi_preprocess(dev_tensor(img), dev_tensor(boxes), size=size, dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        want = ora.roi_preprocess(img, boxes, size=size)
+        g = got.float().cpu().numpy().astype(np.float64)
+        w16 = ora.round_bf16(want)
+        assert np.all(np.abs(g - w16) <= bf16_ulp(w16) + TOL_F32), size
+        assert np.mean(g == w16) > 0.99, size
+        del got, g, want, w16
+
+
 def test_roi_preprocess_full_workload_sampled(gkd, ora):
     """256 detector boxes on a 1920x1080 image, launched as the benchmark
     launches them; the oracle recomputes 12 sampled boxes."""
@@ -112,10 +131,11 @@ def test_roi_preprocess_writes_every_value_once(gkd):
     img = rng.integers(0, 256, (40, 50, 3)).astype(np.uint8)
     boxes = np.array([(0, 0, 50, 40), (60, 0, 70, 10), (3, 3, 9, 30)], np.int32)
     for size in (30, 31):
-        out = torch.full((3, 3, size, size), float("nan"), device="cuda")
-        gkd.roi_preprocess(dev_tensor(img), dev_tensor(boxes), size=size, out=out)
-        torch.cuda.synchronize()
-        assert not torch.isnan(out).any()
+        for dt in (torch.float32, torch.bfloat16):
+            out = torch.full((3, 3, size, size), float("nan"), device="cuda", dtype=dt)
+            gkd.roi_preprocess(dev_tensor(img), dev_tensor(boxes), size=size, dtype=dt, out=out)
+            torch.cuda.synchronize()
+            assert not torch.isnan(out).any(), (size, dt)
 
 
 def test_roi_backproject_matches_oracle(gkd, ora):
