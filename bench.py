@@ -874,7 +874,8 @@ def main():
 
     achieved = heat_bytes / (hm_ms * 1e-3) / 1e9
     copy_gbs = copy_bandwidth(torch)
-    traffic = read_traffic()
+    # the counter summary covers the long-tail batch only
+    traffic = read_traffic() if args.workload == "longtail_bf16" else None
 
     cpu = None
     parity = None

@@ -404,30 +404,52 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  switch (n) {
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 15: wait_vmcnt<15>(); break;
-    case 16: wait_vmcnt<16>(); break;
-    case 17: wait_vmcnt<17>(); break;
-    case 18: wait_vmcnt<18>(); break;
-    case 19: wait_vmcnt<19>(); break;
-    case 20: wait_vmcnt<20>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 7]. The count is an
+// immediate, so a three-level branch tree over the bits of n picks one of
+// eight waits (a switch compiles to a structurized chain several times as
+// long, on the K loop's critical path).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  asm volatile(
+      "s_bitcmp1_b32 %0, 2\n\t"
+      "s_cbranch_scc1 .Lw1_%=\n\t"
+      "s_bitcmp1_b32 %0, 1\n\t"
+      "s_cbranch_scc1 .Lw01_%=\n\t"
+      "s_bitcmp1_b32 %0, 0\n\t"
+      "s_cbranch_scc1 .Lw001_%=\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw001_%=:\n\t"
+      "s_waitcnt vmcnt(1)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw01_%=:\n\t"
+      "s_bitcmp1_b32 %0, 0\n\t"
+      "s_cbranch_scc1 .Lw011_%=\n\t"
+      "s_waitcnt vmcnt(2)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw011_%=:\n\t"
+      "s_waitcnt vmcnt(3)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw1_%=:\n\t"
+      "s_bitcmp1_b32 %0, 1\n\t"
+      "s_cbranch_scc1 .Lw11_%=\n\t"
+      "s_bitcmp1_b32 %0, 0\n\t"
+      "s_cbranch_scc1 .Lw101_%=\n\t"
+      "s_waitcnt vmcnt(4)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw101_%=:\n\t"
+      "s_waitcnt vmcnt(5)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw11_%=:\n\t"
+      "s_bitcmp1_b32 %0, 0\n\t"
+      "s_cbranch_scc1 .Lw111_%=\n\t"
+      "s_waitcnt vmcnt(6)\n\t"
+      "s_branch .Lwe_%=\n"
+      ".Lw111_%=:\n\t"
+      "s_waitcnt vmcnt(7)\n"
+      ".Lwe_%=:"
+      :
+      : "s"(n)
+      : "memory", "scc");
 }
 
 // Workgroup barrier without a memory fence (a fence would also drain the
@@ -445,39 +467,23 @@ __device__ __forceinline__ void lds_barrier() {
 // whole 1 KiB blocks (one load instruction: 64 lanes x 16 B, lane order).
 // Feature block q goes to wave q % 12; kernel-row blocks continue the same
 // round robin after the feature blocks, so no wave issues more than
-// ceil(blocks / 12) loads per step. Per lane and instruction: a source kind
-// (feature map, visual or text kernel rows, or a stand-in that is never
-// read) and an element offset.
-enum : uint32_t { kSrcF = 0, kSrcV = 1, kSrcT = 2, kSrcJunk = 3 };
+// ceil(blocks / 12) loads per step. Per lane and instruction: the source
+// address of step 0 (features) or of steps 0 and 1 (kernel rows); a step
+// adds one wave-uniform byte offset. Slots that are never read (row pads,
+// past the plan) load the crop's first feature bytes plus that offset,
+// which stay inside the crop's feature map at every step, so every lane
+// issues every load with no exec masking and no per-step address selection.
 struct DmaPlan {
-  uint32_t off[kMaxDma];
-  uint32_t kinds;  // 2 bits per instruction
-  uint32_t live;   // bit i: this lane loads in instruction i (lane 0 always)
-  uint32_t live1;  // the same for a pair that holds one K step only (odd step count)
-  uint32_t second; // bit i: this lane's slot holds the pair's second step
-  int nf;          // feature loads of this wave per step (instructions 0 .. nf-1)
-  int na;          // kernel-row loads per step (instructions nf .. nf+na-1)
-  int qa0;         // first kernel-row block of this wave
+  uint64_t src[kMaxDma];  // per-lane source address of instruction i at step 0
+  uint32_t second;        // bit i: this lane's slot holds the pair's second step
+  int nf;                 // feature loads of this wave per step (instructions 0 .. nf-1)
+  int na;                 // kernel-row loads per step (instructions nf .. nf+na-1)
+  int qa0;                // first kernel-row block of this wave
 };
 struct DmaBases {
-  const uint16_t* F;   // the crop's feature map
-  const uint16_t* kv;  // the crop's visual kernel rows, or combined hi parts (or F)
-  const uint16_t* kt;  // the crop's text kernel rows, or combined lo parts (or F)
-  size_t fstep;        // feature elements per K step: 32 * S
+  const uint16_t* F;   // the crop's feature map (also the stand-in source)
+  size_t fstep_bytes;  // feature bytes per K step: 64 S (channel rows) or 64 (tokens)
 };
-
-__device__ __forceinline__ uint64_t dma_source(const DmaPlan& pl, const DmaBases& bs, int i,
-                                               int step) {
-  const uint64_t f = (uint64_t)(bs.F + (size_t)step * bs.fstep);
-  const uint64_t v = (uint64_t)(bs.kv + (size_t)step * kKS);
-  const uint64_t t = (uint64_t)(bs.kt + (size_t)step * kKS);
-  const uint64_t j = (uint64_t)bs.F;
-  const uint32_t kind = (pl.kinds >> (2 * i)) & 3u;
-  // branch-free per-lane choice of the source
-  const uint64_t lo = (kind & 1u) ? v : f;
-  const uint64_t hi = (kind & 1u) ? j : t;
-  return ((kind & 2u) ? hi : lo) + 2ull * pl.off[i];
-}
 
 // cache policy of the feature loads: non-temporal (each feature byte is
 // read once, so the stream should not displace what the next passes reuse
@@ -490,10 +496,11 @@ constexpr int kFeatureCpol = 2;
 template <bool TOK>
 __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases& bs,
                                                unsigned char* fs, int wave, int step) {
+  const uint64_t so = (uint64_t)step * bs.fstep_bytes;
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
-    if (i < pl.nf && ((pl.live >> i) & 1u)) {
-      glb_void* src = (glb_void*)dma_source(pl, bs, i, step);
+    if (i < pl.nf) {
+      glb_void* src = (glb_void*)(pl.src[i] + so);
       lds_void* dst = (lds_void*)(fs + (size_t)(wave + kCWaves * i) * 1024);
       if constexpr (TOK)
         __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
@@ -506,15 +513,18 @@ __device__ __forceinline__ void issue_features(const DmaPlan& pl, const DmaBases
 // kernel-row slot as; `last` when step + 1 is past the end
 __device__ __forceinline__ void issue_rows(const DmaPlan& pl, const DmaBases& bs,
                                            unsigned char* as, int step, bool last) {
-  const uint32_t live = last ? pl.live1 : pl.live;
+  const uint64_t so = (uint64_t)step * (kKS * 2);
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i)
-    if (i >= pl.nf && i < pl.nf + pl.na && ((live >> i) & 1u))
-      __builtin_amdgcn_global_load_lds(
-          // in a one-step pair, lane 0's stand-in for a second-step column
-          // loads the crop's first feature bytes instead of past the row
-          (glb_void*)(last && ((pl.second >> i) & 1u) ? (uint64_t)bs.F : dma_source(pl, bs, i, step)),
-          (lds_void*)(as + (size_t)(pl.qa0 + kCWaves * (i - pl.nf)) * 1024), 16, 0, 0);
+    if (i >= pl.nf && i < pl.nf + pl.na) {
+      uint64_t src = pl.src[i] + so;
+      // in a one-step pair, a second-step column would run past the row:
+      // the lane loads the stand-in instead
+      if (last && ((pl.second >> i) & 1u)) src = (uint64_t)bs.F;
+      __builtin_amdgcn_global_load_lds((glb_void*)src,
+                                       (lds_void*)(as + (size_t)(pl.qa0 + kCWaves * (i - pl.nf)) * 1024),
+                                       16, 0, 0);
+    }
 }
 
 // Two channels of the combination w_v k_v + w_t k_t (bf16 pairs, the lower
@@ -605,11 +615,11 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
       // the next) has landed for this wave once at most the loads of the
       // younger steps issued so far remain; step 0's kernel rows were issued
       // after the feature prologue, so step 0 waits for everything
-      int younger = 0;
-      if (k > 0)
-        for (int s = k + 1; s < k + ahead && s < p.nsteps; ++s)
-          younger += pl.nf + ((s & 1) == 0 ? pl.na : 0);
-      wait_vmcnt_upto(younger);
+      // (ahead is 1 or 2: at most the next step's loads, <= kMaxDma)
+      static_assert(kStages == 3 && kMaxDma <= 7, "one younger step of at most 7 loads");
+      const int younger =
+          k > 0 && ahead == 2 && k + 1 < p.nsteps ? pl.nf + ((k & 1) ? pl.na : 0) : 0;
+      wait_vmcnt_dyn(younger);
     }
     lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
     if constexpr (COMB) {
@@ -855,50 +865,32 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
 
   DmaBases bs;
   bs.F = tok ? p.query + ((size_t)b * p.tok_T + p.tok_skip) * p.C : p.query + (size_t)b * p.C * p.S;
-  bs.fstep = tok ? (size_t)kKS : (size_t)kKS * p.S;
-  bs.kv = bs.F;
-  bs.kt = bs.F;
+  bs.fstep_bytes = tok ? (size_t)kKS * 2 : (size_t)kKS * p.S * 2;
+  const uint64_t stand_in = (uint64_t)bs.F;
 
   // ---- DMA plan, feature part. Feature slot u < nF: feature row r = u /
   // rs (channel), 16-byte column u % rs (the last one pads the row); past
   // the map: the row's start. Pad slots and slots past the plan are never
-  // read: their lanes issue no load, except lane 0 (a stand-in), so every
-  // wave still issues each instruction and the per-step load counts the K
-  // loop waits on hold. The feature prologue needs no row information, so
-  // it is in flight while the item's rows are selected.
+  // read and load the stand-in. The feature prologue needs no row
+  // information, so it is in flight while the item's rows are selected.
   DmaPlan pl;
   pl.nf = wave < nfi ? (nfi - wave + kCWaves - 1) / kCWaves : 0;
-  pl.kinds = 0;
-  pl.live = 0;
-  pl.live1 = 0;
   pl.second = 0;
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i) {
-    pl.off[i] = 0;
-    if (i >= pl.nf) continue;  // the kernel-row part sets its own bits below
-    uint32_t kind = kSrcJunk, off = 0;
+    pl.src[i] = stand_in;
+    if (i >= pl.nf) continue;  // the kernel-row part fills its own below
     const int u = (wave + kCWaves * i) * kWave + lane_p;
     if (u < nF && tok) {
       // pixel px0 + u / 4, channels 8 (u % 4) .. + 7 of the step; past the
-      // map: junk (the pixels are never read)
+      // map: the stand-in (the pixels are never read)
       const int px = it.px0 + (u >> 2);
-      if (px < p.S) {
-        kind = kSrcF;
-        off = (uint32_t)px * (uint32_t)p.C + 8u * (uint32_t)(u & 3);
-      }
+      if (px < p.S)
+        pl.src[i] = stand_in + 2ull * ((uint32_t)px * (uint32_t)p.C + 8u * (uint32_t)(u & 3));
     } else if (u < nF) {
       const int r = u / it.rs, cc = u - r * it.rs;
       const int px = it.px0 + 8 * cc;
-      if (cc < it.rs - 1) {
-        kind = kSrcF;
-        off = (uint32_t)(r * p.S + (px < p.S ? px : 0));
-      }
-    }
-    pl.off[i] = off;
-    pl.kinds |= kind << (2 * i);
-    if (kind != kSrcJunk || lane_p == 0) {
-      pl.live |= 1u << i;
-      pl.live1 |= 1u << i;
+      if (cc < it.rs - 1) pl.src[i] = stand_in + 2ull * (uint32_t)(r * p.S + (px < p.S ? px : 0));
     }
   }
   issue_features<TOK>(pl, bs, lds, wave, 0);
@@ -962,10 +954,10 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
   // parked in the crop's heatmap rows (row pitch 2 row_f bf16 values)
   const uint16_t* const crop_heat =
       reinterpret_cast<const uint16_t*>(p.heat + (size_t)b * p.R * p.row_f);
-  bs.kv = pre ? crop_heat + 2 * (size_t)p.comb_hi
-              : (has_v ? p.kv + (size_t)b * p.R * p.C : bs.F);
-  bs.kt = pre ? crop_heat + 2 * (size_t)p.comb_lo
-              : (has_t ? p.kt + (size_t)b * p.R * p.C : bs.F);
+  const uint16_t* const rows_v = pre ? crop_heat + 2 * (size_t)p.comb_hi
+                                     : (has_v ? p.kv + (size_t)b * p.R * p.C : bs.F);
+  const uint16_t* const rows_t = pre ? crop_heat + 2 * (size_t)p.comb_lo
+                                     : (has_t ? p.kt + (size_t)b * p.R * p.C : bs.F);
   const uint32_t rpitch = pre ? 2u * (uint32_t)p.row_f : (uint32_t)p.C;
 
   // ---- DMA plan, kernel-row part. Kernel-row slot v < nA: kernel row
@@ -980,7 +972,6 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
 #pragma unroll
   for (int i = 0; i < kMaxDma; ++i) {
     if (i < pl.nf || i >= pl.nf + pl.na) continue;
-    uint32_t kind = kSrcJunk, off = 0;
     const int v = (pl.qa0 + kCWaves * (i - pl.nf)) * kWave + lane_p;
     if (v < nA && v % kRowSlots < kRowSlots - 1) {
       const int ar = v / kRowSlots, ac = v - ar * kRowSlots;
@@ -988,17 +979,12 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
       const bool vis = has_v && mi == 0;
       const bool on = slot < it.nsel && (pre || (vis ? s_mv[slot] : s_mt[slot]));
       const int use = on ? slot : (pre ? 0 : (vis ? first_v : first_t));
-      kind = vis ? kSrcV : kSrcT;
-      off = (uint32_t)s_rows[use] * rpitch + 8 * ac;
+      pl.src[i] = (uint64_t)(vis ? rows_v : rows_t) +
+                  2ull * ((uint32_t)s_rows[use] * rpitch + 8 * ac);
+      // a last pair with one step: the second step's columns are not read
+      // (they would run past the row)
+      if (ac >= 4) pl.second |= 1u << i;
     }
-    pl.off[i] = off;
-    pl.kinds |= kind << (2 * i);
-    if (kind != kSrcJunk || lane_p == 0) pl.live |= 1u << i;
-    // a last pair with one step: the second step's columns are not read
-    // (they would run past the row)
-    const bool second = kind != kSrcJunk && v % kRowSlots >= 4;
-    if ((kind != kSrcJunk && !second) || lane_p == 0) pl.live1 |= 1u << i;
-    if (second) pl.second |= 1u << i;
   }
   // the rest of the prologue: features of step 1 (items that load two
   // steps ahead), then the kernel rows of steps 0 and 1, so the K loop
