@@ -1190,30 +1190,53 @@ __global__ __launch_bounds__(kEThreads) void expand_kernel(ExpandParams p) {
     }
   }
 
-  // this wave's row: the rank-th valid row of the crop
+  // this wave's row: the rank-th valid row of the crop. The masks of two
+  // 64-row chunks are requested together (clamped indices, so every load is
+  // in bounds and in flight before the first ballot).
   int rank = ic.item * p.wpg + wave;
   int row = -1;
-  for (int base = 0; base < p.R; base += kWave) {
-    const int r = base + lane;
-    const bool v = r < p.R && ((mv && mv[r]) || (mt && mt[r]));
-    const uint64_t bal = __ballot(v);
-    const int cnt = __popcll(bal);
-    if (rank < cnt) {
-      const int below = __popcll(bal & ((1ull << lane) - 1ull));
-      const uint64_t hit = __ballot(v && below == rank);
-      row = base + __builtin_ctzll(hit);
-      break;
+  for (int base = 0; base < p.R && row < 0; base += 2 * kWave) {
+    uint8_t x[2], y[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = min(base + h * kWave + lane, p.R - 1);
+      x[h] = mv ? mv[q] : 0;
+      y[h] = mt ? mt[q] : 0;
     }
-    rank -= cnt;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c0 = base + h * kWave;
+      const bool v = c0 + lane < p.R && (x[h] | y[h]);
+      const uint64_t bal = __ballot(v);
+      const int cnt = __popcll(bal);
+      if (row < 0) {
+        if (rank < cnt) {
+          const int below = __popcll(bal & ((1ull << lane) - 1ull));
+          const uint64_t hit = __ballot(v && below == rank);
+          row = c0 + __builtin_ctzll(hit);
+        } else {
+          rank -= cnt;
+        }
+      }
+    }
   }
   if (row < 0) return;
 
   float* out = p.heat + ((size_t)b * p.R + row) * p.row_f;
   float* P = lds_p + (size_t)wave * p.S;
-  // the parked low-res map -> LDS (this wave only); every load has returned
-  // before the first store below can overwrite it
-  for (int v = lane; 4 * v < p.S; v += kWave)
-    reinterpret_cast<f32x4*>(P)[v] = reinterpret_cast<const f32x4*>(out)[v];
+  // the parked low-res map -> LDS (this wave only), four 16-byte loads per
+  // lane in flight at a time; every load has returned before the first
+  // store below can overwrite it
+  const int nv = p.S / 4;
+  for (int v0 = 0; v0 < nv; v0 += 4 * kWave) {
+    f32x4 t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      t[i] = reinterpret_cast<const f32x4*>(out)[min(v0 + i * kWave + lane, nv - 1)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (v0 + i * kWave + lane < nv) reinterpret_cast<f32x4*>(P)[v0 + i * kWave + lane] = t[i];
+  }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
   const RowGeom g{p.H, p.W, p.S, p.Ho, p.Wo, p.magic_w};
