@@ -613,12 +613,11 @@ __device__ __forceinline__ void contract_item(const ContractParams& p, unsigned 
     {
       // step k (features, and with an even step the kernel rows of it and
       // the next) has landed for this wave once at most the loads of the
-      // younger steps issued so far remain; step 0's kernel rows were issued
-      // after the feature prologue, so step 0 waits for everything
+      // younger steps issued so far remain: every wave issues its loads in
+      // step order, the prologue included, so those are step k + 1's
       // (ahead is 1 or 2: at most the next step's loads, <= kMaxDma)
       static_assert(kStages == 3 && kMaxDma <= 7, "one younger step of at most 7 loads");
-      const int younger =
-          k > 0 && ahead == 2 && k + 1 < p.nsteps ? pl.nf + ((k & 1) ? pl.na : 0) : 0;
+      const int younger = ahead == 2 && k + 1 < p.nsteps ? pl.nf + ((k & 1) ? pl.na : 0) : 0;
       wait_vmcnt_dyn(younger);
     }
     lds_barrier();  // everyone's step k landed; the slots of step k-1 are free
@@ -986,16 +985,16 @@ __global__ __launch_bounds__(kCThreads) void contract_kernel(ContractParams p) {
       if (ac >= 4) pl.second |= 1u << i;
     }
   }
-  // the rest of the prologue: features of step 1 (items that load two
-  // steps ahead), then the kernel rows of steps 0 and 1, so the K loop
-  // waits for everything at step 0. Items with few kernel rows move fewer
-  // bytes per step; loading them only one step ahead leaves the heavier
-  // items of the batch a larger share of the memory bandwidth, so all
-  // items finish closer together.
+  // the rest of the prologue: the kernel rows of steps 0 and 1, then the
+  // features of step 1 (items that load two steps ahead), so step 0 waits
+  // only for its own loads and is not queued behind step 1's. Items with
+  // few kernel rows move fewer bytes per step; loading them only one step
+  // ahead leaves the heavier items of the batch a larger share of the
+  // memory bandwidth, so all items finish closer together.
   it.ahead = it.arows <= p.light_arows ? 1 : kStages - 1;
-  if (it.ahead > 1 && p.nsteps > 1) issue_features<TOK>(pl, bs, lds + (size_t)it.fbytes, wave, 1);
   unsigned char* const aring = lds + (size_t)kStages * it.fbytes;
   issue_rows(pl, bs, aring, 0, p.nsteps == 1);
+  if (it.ahead > 1 && p.nsteps > 1) issue_features<TOK>(pl, bs, lds + (size_t)it.fbytes, wave, 1);
 
   const int upw = (it.MH * it.ng + kCWaves - 1) / kCWaves;
   if (pre)
