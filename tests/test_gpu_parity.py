@@ -692,7 +692,7 @@ def _tokens(q, skip, rng):
 
 @pytest.mark.parametrize("skip", [0, 5])
 @pytest.mark.parametrize("shape", [(3, 64, 8, 8, 16), (2, 256, 24, 24, 40), (1, 64, 32, 32, 6),
-                                   (3, 256, 4, 4, 12), (2, 32, 6, 8, 200)])
+                                   (3, 256, 4, 4, 12), (2, 32, 6, 8, 200), (2, 96, 8, 8, 24)])
 def test_query_tokens_layout(gkd, ora, shape, skip):
     """GKD_QUERY_TOKENS: the token sequence [B, skip + H*W, C] gives, bit
     for bit, the results of the same call on [B, C, H, W] (heatmaps,
