@@ -515,6 +515,43 @@ def kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows, n=20):
     return res
 
 
+def kg_highres_mode(torch, gkd, n=10):
+    """The kernel-generation transformer on the high-resolution batch (B=128,
+    80 text-prompted rows a crop, C=1024, a 48x48 query: 2304 cross-attention
+    keys a crop), 2 blocks, d_ff 1024, synthetic weights: the call alone."""
+    import gkdsynth
+    d = gkdsynth.make("highres_bf16")
+    B, C, H, W, R = d["B"], d["C"], d["H"], d["W"], d["R"]
+    F, nb = 1024, 2
+    q = torch.from_numpy(d["query"]).to("cuda").to(torch.bfloat16)
+    kt = torch.from_numpy(np.nan_to_num(d["kern_txt"])).to("cuda").to(torch.bfloat16)
+    mt = torch.from_numpy(d["mask_txt"]).to("cuda")
+    wt = torch.from_numpy(gkdsynth.kg_weights(C, F, nb, seed=5)).to("cuda").to(torch.bfloat16)
+    out = torch.empty((2, B, R, C), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gkd.kg_workspace_size(B, C, H, W, R, F), dtype=torch.uint8, device="cuda")
+    call = lambda: gkd.kg_transformer(q, wt, kern_txt=kt, mask_txt=mt, n_blocks=nb, d_ff=F,
+                                      out=out, workspace=ws)
+    for _ in range(2):
+        call()
+    evs = [[TimingEvent(torch) for _ in range(2)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for k in range(n):
+        evs[k][0].record()
+        call()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    flp = kg_flops_prompted(np.zeros_like(d["mask_txt"]), d["mask_txt"], C, H * W, F, nb)
+    return {"note": "kernel-generation transformer on the high-resolution batch (text "
+                    "prompts, 48x48 query), synthetic weights, call alone; not the headline",
+            "shape": {"B": B, "slots": 2 * R, "C": C, "HW": H * W, "d_ff": F, "blocks": nb,
+                      "prompted_slots": int(2 * (d["mask_txt"] > 0).sum())},
+            "call_ms": round(ms, 4),
+            "alg_tflop": round(flp / 1e12, 4),
+            "tflops": round(flp / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flp / (ms * 1e-3) / 1e12 / 2500.0, 4)}
+
+
 def config_mode(torch, gkd, name, n=50, flush=None):
     """One workload's heatmap call at its own shape, alone: warm (calls back
     to back) and cold (a 1 GiB write between calls, so no input byte is
@@ -842,6 +879,8 @@ def main():
         if has_vis and has_txt and q.dtype == torch.bfloat16:
             d["support_t"] = sup
             kgr = kg_mode(torch, gkd, d, protos, mv, kt, mt, q, kp, rows)
+        log("[bench] kernel-generation transformer, high-resolution query")
+        kgh = kg_highres_mode(torch, gkd)
         log("[bench] small-config latency")
         lat = latency_mode(torch, gkd)
         log("[bench] token-layout query")
@@ -851,6 +890,7 @@ def main():
         modes = {
             "configs": cfgs,
             "kg_transformer": kgr,
+            "kg_transformer_highres": kgh,
             "latency_small": lat,
             "query_tokens": toks,
             "longtail_dense": dense,

@@ -334,9 +334,10 @@ GKD_API gkd_status gkd_roi_backproject(const float *xy, const int32_t *boxes, in
  *              workspace must not overlap.
  * dtype must be GKD_DTYPE_BF16 (matrix operands in bfloat16, accumulation,
  * softmax, LayerNorm and the residual stream in float32). Limits: C % 64
- * == 0, d_ff % 64 == 0, 1 <= n_blocks <= 64, 2R <= 576, H*W <= 576 (the
- * attention holds all scores of a row in registers), else
- * GKD_ERR_UNSUPPORTED. All arrays but the masks 16-byte aligned (else
+ * == 0, d_ff % 64 == 0, 1 <= n_blocks <= 64, 2R <= 576 (the
+ * self-attention holds all scores of a row in registers; the
+ * cross-attention streams the H*W keys, so H*W is limited only by the
+ * element counts below), else GKD_ERR_UNSUPPORTED. All arrays but the masks 16-byte aligned (else
  * GKD_ERR_ALIGN); workspace_bytes too small gives GKD_ERR_VALUE. flags: 0
  * or GKD_QUERY_TOKENS | GKD_QUERY_SKIP(n).
  */

@@ -303,9 +303,9 @@ gkd_status kg_check(const char* fn, const void* kern_vis, const uint8_t* mask_vi
   if (B < 0 || R < 0 || C < 1 || H < 1 || W < 1 || d_ff < 1 || n_blocks < 1)
     return fail(GKD_ERR_SHAPE, "%s: bad shape B=%d C=%d H=%d W=%d R=%d d_ff=%d "
                 "n_blocks=%d", fn, B, C, H, W, R, d_ff, n_blocks);
-  if (C % 64 != 0 || d_ff % 64 != 0 || n_blocks > 64 || 2LL * R > 576 || (long long)H * W > 576)
+  if (C % 64 != 0 || d_ff % 64 != 0 || n_blocks > 64 || 2LL * R > 576)
     return fail(GKD_ERR_UNSUPPORTED, "%s: needs C %% 64 == 0, d_ff %% 64 == 0, "
-                "n_blocks <= 64, 2R <= 576 and H*W <= 576", fn);
+                "n_blocks <= 64 and 2R <= 576", fn);
   const long long HW = (long long)H * W, M = 2LL * B * R;
   if (M * (C > d_ff ? C : d_ff) > kMaxElems || B * (HW + skip) * C > kMaxElems ||
       (long long)C * C * 8 + 2LL * C * d_ff > kMaxElems / n_blocks)

@@ -263,7 +263,6 @@ def kg(lib, vis=A, mv=A2, txt=None, mt=None, query=A3, B=2, C=128, H=24, W=24, R
     (dict(C=96), UNSUP),
     (dict(F=100), UNSUP),
     (dict(R=289), UNSUP),                      # 2R > 576
-    (dict(H=25), UNSUP),                       # H*W > 576
     (dict(nb=0), SHAPE),
     (dict(nb=65), UNSUP),
     (dict(B=-1), SHAPE),

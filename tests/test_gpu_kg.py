@@ -96,10 +96,13 @@ def check(got, want):
 
 
 @pytest.mark.parametrize("B,R,C,H,W,F", [(3, 7, 128, 5, 7, 192), (2, 40, 192, 9, 9, 128),
-                                         (1, 3, 64, 1, 1, 64)])
+                                         (1, 3, 64, 1, 1, 64), (2, 9, 128, 48, 48, 128),
+                                         (1, 5, 64, 25, 37, 64)])
 def test_kg_matches_oracle_small(gkd, okg, B, R, C, H, W, F):
-    """Ragged slot counts (14, 80, 6 of 64-query tiles), ragged key tails
-    (35, 81, 1 keys) and tiles past M and N."""
+    """Ragged slot counts (14, 80, 6, 18, 10 slots against 16-query tiles),
+    ragged key tails (35, 81, 1 keys; 2304 and 925 keys stream through the
+    cross-attention's 64-key chunks in 36 and 15 chunks, the last one
+    partial) and tiles past M and N."""
     vis, mv, txt, mt, q, w = case(B * 100 + R, B, R, C, H, W, F, 2)
     mv[0, -1] = mt[0, -1] = 0   # a padding row
     print(f"[kg] small B={B} R={R} C={C} HW={H * W} F={F}", flush=True)
@@ -147,4 +150,18 @@ def test_kg_full_size_sampled(gkd, okg):
     for i in (0, 101, 255):
         want = okg.kg_transformer(vis[i:i + 1], mv[i:i + 1], txt[i:i + 1], mt[i:i + 1],
                                   q[i:i + 1], w, 2, F)
+        check(a[i:i + 1], want)
+
+
+def test_kg_highres_query_sampled(gkd, okg):
+    """Crops of the high-resolution batch's shape: all 80 rows text-prompted
+    (the 80 visual slots unprompted), C=1024, a 48x48 query (2304
+    cross-attention keys a crop), d_ff=1024, 2 blocks; 32 crops, the oracle
+    recomputes 2 sampled ones."""
+    B, R, C, H, W, F = 32, 80, 1024, 48, 48, 1024
+    vis, mv, txt, mt, q, w = case(77, B, R, C, H, W, F, 2, p_vis=0.0, p_txt=1.0)
+    print("[kg] high-resolution query", flush=True)
+    a = run(gkd, vis, mv, txt, mt, q, w, 2, F, modalities="text")
+    for i in (0, 31):
+        want = okg.kg_transformer(None, None, txt[i:i + 1], mt[i:i + 1], q[i:i + 1], w, 2, F)
         check(a[i:i + 1], want)
