@@ -1149,6 +1149,8 @@ __global__ __launch_bounds__(kPWaves * kWave) void row_prep_kernel(PrepParams p)
 // ---------------------------------------------------------------------------
 constexpr int kEWaves = 4;
 constexpr int kEThreads = kEWaves * kWave;
+constexpr long long kExpandCapRows = 8192;  // B * R from which the expand's residency is capped
+constexpr size_t kExpandCapLds = 64 * 1024; // LDS of an expand workgroup then: two fit a CU (160 KiB)
 
 struct ExpandParams {
   const uint8_t* mv;
@@ -1292,6 +1294,13 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps, bool
   sp.contract_lds = max_lds <= kContractLds ? kContractLds : max_lds;
   sp.wpg = S <= 4096 ? kEWaves : 1;
   sp.expand_lds = (size_t)sp.wpg * S * sizeof(float);
+  // a batch with many rows: at most two expand workgroups (eight waves) a
+  // CU, by their LDS request. The heatmap rows are written one wave each,
+  // and fewer rows in flight at once store faster (long-tail and dense
+  // batches 2-4 us, the 192x192 batch 6 us a call); a small batch keeps
+  // every row in flight.
+  if ((long long)B * R >= kExpandCapRows && sp.expand_lds < kExpandCapLds)
+    sp.expand_lds = kExpandCapLds;
   sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kContractLds &&
           sp.expand_lds <= 64 * 1024 && (!whole_maps || sp.nchunks == 1);
   return sp;
