@@ -1149,8 +1149,15 @@ __global__ __launch_bounds__(kPWaves * kWave) void row_prep_kernel(PrepParams p)
 // ---------------------------------------------------------------------------
 constexpr int kEWaves = 4;
 constexpr int kEThreads = kEWaves * kWave;
-constexpr long long kExpandCapRows = 8192;  // B * R from which the expand's residency is capped
-constexpr size_t kExpandCapLds = 64 * 1024; // LDS of an expand workgroup then: two fit a CU (160 KiB)
+// A batch with many rows caps the expand workgroups resident on a CU by
+// their LDS request (a CU holds 160 KiB). Each heatmap row is written by one
+// wave, and fewer rows in flight at once store faster: two workgroups (eight
+// waves) a CU for rows up to 96 KB, one for larger rows (the 192x192 float32
+// maps). A small batch keeps every row in flight.
+constexpr long long kExpandCapRows = 8192;    // B * R from which the residency is capped
+constexpr size_t kExpandLds2 = 64 * 1024;     // two workgroups fit a CU, three do not
+constexpr size_t kExpandLds1 = 96 * 1024;     // one workgroup a CU
+constexpr size_t kExpandBigRow = 96 * 1024;   // heatmap row bytes above which one is resident
 
 struct ExpandParams {
   const uint8_t* mv;
@@ -1294,13 +1301,6 @@ StreamPlan plan_heatmap_stream(int B, int C, int S, int R, bool whole_maps, bool
   sp.contract_lds = max_lds <= kContractLds ? kContractLds : max_lds;
   sp.wpg = S <= 4096 ? kEWaves : 1;
   sp.expand_lds = (size_t)sp.wpg * S * sizeof(float);
-  // a batch with many rows: at most two expand workgroups (eight waves) a
-  // CU, by their LDS request. The heatmap rows are written one wave each,
-  // and fewer rows in flight at once store faster (long-tail and dense
-  // batches 2-4 us, the 192x192 batch 6 us a call); a small batch keeps
-  // every row in flight.
-  if ((long long)B * R >= kExpandCapRows && sp.expand_lds < kExpandCapLds)
-    sp.expand_lds = kExpandCapLds;
   sp.ok = ceil_div(max_instr, kCWaves) <= kMaxDma && sp.contract_lds <= kContractLds &&
           sp.expand_lds <= 64 * 1024 && (!whole_maps || sp.nchunks == 1);
   return sp;
@@ -1409,11 +1409,16 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   ep.corners = a.corners;
   ep.xy = a.xy;
   ep.score = a.score;
+  size_t elds = sp.expand_lds;
+  if ((long long)a.B * a.R >= kExpandCapRows) {
+    const size_t cap = row_f * sizeof(float) > kExpandBigRow ? kExpandLds1 : kExpandLds2;
+    if (elds < cap) elds = cap;
+  }
   const long long egrid = crops_pad * ep.groups_per_crop;
   if (egrid > INT_MAX) return hipErrorInvalidConfiguration;
 #define GKD_EXPAND(SW, BF, UPC)                                                              \
   hipLaunchKernelGGL((expand_kernel<SW, BF, UPC>), dim3((unsigned)egrid), dim3(kEThreads),   \
-                     sp.expand_lds, stream, ep)
+                     elds, stream, ep)
   if (a.up_corners) {
     if (a.heat_bf16) GKD_EXPAND(false, true, true);
     else GKD_EXPAND(false, false, true);
