@@ -1151,13 +1151,16 @@ constexpr int kEWaves = 4;
 constexpr int kEThreads = kEWaves * kWave;
 // A batch with many rows caps the expand workgroups resident on a CU by
 // their LDS request (a CU holds 160 KiB). Each heatmap row is written by one
-// wave, and fewer rows in flight at once store faster: two workgroups (eight
-// waves) a CU for rows up to 96 KB, one for larger rows (the 192x192 float32
-// maps). A small batch keeps every row in flight.
+// wave, and fewer rows in flight at once store faster: three workgroups
+// (twelve waves) a CU for rows up to 24 KB (96x96 bfloat16 maps), two for
+// rows up to 96 KB, one for larger rows (the 192x192 float32 maps). A small
+// batch keeps every row in flight.
 constexpr long long kExpandCapRows = 8192;    // B * R from which the residency is capped
-constexpr size_t kExpandLds2 = 64 * 1024;     // two workgroups fit a CU, three do not
-constexpr size_t kExpandLds1 = 96 * 1024;     // one workgroup a CU
-constexpr size_t kExpandBigRow = 96 * 1024;   // heatmap row bytes above which one is resident
+constexpr size_t kExpandLds3 = 52 * 1024;     // three workgroups fit a CU, four do not
+constexpr size_t kExpandLds2 = 64 * 1024;     // two fit, three do not
+constexpr size_t kExpandLds1 = 96 * 1024;     // one
+constexpr size_t kExpandSmallRow = 24 * 1024; // heatmap row bytes up to which three are resident
+constexpr size_t kExpandBigRow = 96 * 1024;   // row bytes above which one is
 
 struct ExpandParams {
   const uint8_t* mv;
@@ -1411,7 +1414,10 @@ hipError_t launch_heatmap_stream(const HeatmapArgs& a, hipStream_t stream) {
   ep.score = a.score;
   size_t elds = sp.expand_lds;
   if ((long long)a.B * a.R >= kExpandCapRows) {
-    const size_t cap = row_f * sizeof(float) > kExpandBigRow ? kExpandLds1 : kExpandLds2;
+    const size_t row_bytes = row_f * sizeof(float);
+    const size_t cap = row_bytes > kExpandBigRow     ? kExpandLds1
+                       : row_bytes > kExpandSmallRow ? kExpandLds2
+                                                     : kExpandLds3;
     if (elds < cap) elds = cap;
   }
   const long long egrid = crops_pad * ep.groups_per_crop;
